@@ -1,0 +1,105 @@
+"""Seeded synthetic inputs for batched LU / solve.
+
+This module only draws numbers and lays them out in memory; it holds none of
+the factorisation's arithmetic, so both the CPU oracle side and the GPU side
+may use it without sharing any step of the method.
+
+Layout: every matrix is column-major; element (i, j) of matrix b sits at
+``b*stride + i + j*ld`` of a flat 1-D buffer.  The workloads follow the five
+shapes the BatchLAS pages time (LU page and Blackwell page): small float
+systems in the register tier, a complex n = 64 system in the work-group tier,
+a double n = 256 and a float n = 1024 system in the blocked tier.  Entries are
+iid uniform[-1, 1] (complex: real and imaginary parts drawn as separate
+blocks), except the n = 1024 workload, which draws N(0, 1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+SEED_BASE = 20261202
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: type
+    n: int
+    nrhs: int
+    batch: int
+    dist: str           # "uniform" (iid U[-1, 1]) or "normal" (iid N(0, 1))
+    op: str             # "gesv", or "getrf+getrs"
+    index: int          # 1-based position, sets the seed
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.index
+
+
+WORKLOADS = {
+    "sgesv_n16_b1024": Workload("sgesv_n16_b1024", np.float32, 16, 1, 1024, "uniform", "gesv", 1),
+    "sgesv_n32_r8_b32768": Workload("sgesv_n32_r8_b32768", np.float32, 32, 8, 32768, "uniform", "gesv", 2),
+    "cgesv_n64_r16_b8192": Workload("cgesv_n64_r16_b8192", np.complex64, 64, 16, 8192, "uniform", "gesv", 3),
+    "dgesv_n256_b1024": Workload("dgesv_n256_b1024", np.float64, 256, 1, 1024, "uniform", "gesv", 4),
+    "sgetrf_sgetrs_n1024_r32_b64": Workload("sgetrf_sgetrs_n1024_r32_b64", np.float32, 1024, 32, 64, "normal",
+                                            "getrf+getrs", 5),
+}
+
+
+def draw(rng: np.random.Generator, dtype, size: int, dist: str = "uniform") -> np.ndarray:
+    """``size`` iid entries of ``dtype``; complex draws the real block first."""
+    dt = np.dtype(dtype)
+    if dt.kind == "c":
+        real = np.float32 if dt == np.complex64 else np.float64
+        re = draw(rng, real, size, dist)
+        im = draw(rng, real, size, dist)
+        out = np.empty(size, dt)
+        out.real, out.imag = re, im
+        return out
+    if dist == "uniform":
+        return rng.uniform(-1.0, 1.0, size).astype(dt)
+    if dist == "normal":
+        if dt == np.float32:
+            return rng.standard_normal(size, dtype=np.float32)
+        return rng.standard_normal(size).astype(dt)
+    raise ValueError(dist)
+
+
+def dense_problem(w: Workload, batch: int | None = None):
+    """(A, B) as flat buffers with ld = n and strides n*n and n*nrhs.
+
+    ``batch`` below the workload's batch takes the leading matrices of the
+    same draw (A for all matrices is drawn before B)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    A = draw(rng, w.dtype, w.batch * w.n * w.n, w.dist)
+    B = draw(rng, w.dtype, w.batch * w.n * w.nrhs, w.dist)
+    if batch is not None and batch < w.batch:
+        A = A[: batch * w.n * w.n].copy()
+        B = B[: batch * w.n * w.nrhs].copy()
+    return A, B
+
+
+def random_problem(seed: int, dtype, n: int, nrhs: int, batch: int, dist: str = "uniform"):
+    """Same recipe as the named workloads, any shape."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    A = draw(rng, dtype, batch * n * n, dist)
+    B = draw(rng, dtype, batch * n * nrhs, dist)
+    return A, B
+
+
+def relayout(flat: np.ndarray, rows: int, cols: int, batch: int, ld_in: int, stride_in: int,
+             ld_out: int, stride_out: int, poison=None) -> np.ndarray:
+    """Copy a batch of rows x cols column-major matrices into a new buffer with
+    another leading dimension / batch stride; the gaps hold ``poison``."""
+    if ld_out < rows or (cols > 0 and stride_out < ld_out * (cols - 1) + rows):
+        raise ValueError("output layout too small")
+    total = stride_out * batch if batch > 0 else 0
+    out = np.empty(max(total, 1), flat.dtype)
+    out[:] = poison if poison is not None else 0
+    for b in range(batch):
+        for j in range(cols):
+            src = b * stride_in + j * ld_in
+            dst = b * stride_out + j * ld_out
+            out[dst: dst + rows] = flat[src: src + rows]
+    return out[:total] if total > 0 else out[:0]
