@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched gesv hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one batched gesv call (factor + forward + back substitution for
+every matrix of the batch) on synthetic inputs already resident in HBM.  The
+factorisation is in place, so every step gets its own pre-copied input set
+(copies happen before the timed region).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import lu_inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+FP32_ALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop x 2.4 GHz, no packed FP32
+FP64_PEAK_TFLOPS = 78.6
+METRIC = "batched gesv matrices/s + GFLOP/s (n=32 f32, n=256 f64), % of roofline"
+KERNEL_SOURCES = {
+    "register": ["dense_linear_algebra_amd/csrc/register_lu_kernel.h", "dense_linear_algebra_amd/csrc/device_ops.h"],
+}
+
+
+def algorithmic_bytes(w) -> int:
+    """A read and written, B read and X written, ipiv and info written."""
+    es = np.dtype(w.dtype).itemsize
+    return es * (2 * w.n * w.n + 2 * w.n * w.nrhs) + 4 * w.n + 4
+
+
+def algorithmic_flops(w) -> float:
+    """2/3 n^3 + 2 n^2 nrhs per matrix; complex counts 4 real flops per op."""
+    f = 2.0 / 3.0 * w.n ** 3 + 2.0 * w.n ** 2 * w.nrhs
+    return f * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0)
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(kind, []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_gesv_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except Exception:
+        return None
+    if d.get("source_hash") != source_hash(kind):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, A, B, budget_s: float = 10.0):
+    """The oracle (as is) on host cores: whole-batch gesv repeated until about
+    budget_s of wall time has elapsed."""
+    import oracle
+    reps, used, t_total, mats = 0, 0, 0.0, 0
+    while t_total < budget_s and reps < 50:
+        a, b = A.copy(), B.copy()
+        t0 = time.perf_counter()
+        _, _, _, used = oracle.gesv(a, w.n, w.n, w.n * w.n, b, w.nrhs, w.n, w.n * w.nrhs, w.batch)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        mats += w.batch
+    return {"value": mats / t_total, "unit": "matrices/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{reps} x the full batch of {w.batch} ({t_total:.1f} s wall)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sgesv_n32_r8_b32768", choices=sorted(lu_inputs.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one plain device copy of this size first (reference for HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: every matrix is independent, so more GPUs would each "
+              f"take batch/{args.gpus} matrices with no communication; --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_linear_algebra_amd as lib
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib.load()
+    w = lu_inputs.WORKLOADS[args.workload]
+    A, B = lu_inputs.dense_problem(w)
+    dev = torch.device("cuda:0")
+    t = lib.dtype_code(A.dtype)
+    hA = torch.from_numpy(A)
+    hB = torch.from_numpy(B)
+    nsets = args.warmup + args.steps
+    sets = []
+    for _ in range(nsets):
+        sets.append((hA.to(dev), hB.to(dev)))
+    ipiv = torch.empty(w.batch * w.n, dtype=torch.int32, device=dev)
+    info = torch.empty(w.batch, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    tier = lib.batchlu_select_tier(t, 2, w.n, w.nrhs, w.batch)
+
+    def step(i):
+        dA, dB = sets[i]
+        lib.batchlu_gesv(t, w.n, w.nrhs, dA, w.n, w.n * w.n, ipiv, w.n, dB, w.n, w.n * w.nrhs, info, w.batch,
+                         stream=stream)
+
+    if args.copy_probe_mb > 0:
+        src = torch.empty(args.copy_probe_mb << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # quick parity sample of the first warm-up output against the oracle
+    parity = None
+    if args.warmup > 0:
+        import oracle
+        k = min(16, w.batch)
+        a0 = A[: k * w.n * w.n].copy()
+        b0 = B[: k * w.n * w.nrhs].copy()
+        oip, oinfo, _, _ = oracle.gesv(a0, w.n, w.n, w.n * w.n, b0, w.nrhs, w.n, w.n * w.nrhs, k)
+        gA0 = sets[0][0][: k * w.n * w.n].cpu().numpy()
+        parity = {"sampled_matrices": k,
+                  "lu_bitwise_equal": bool(np.array_equal(gA0.view(np.uint8), a0.view(np.uint8)))}
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.warmup, nsets):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    ms_per_step = wall * 1e3 / args.steps
+    mats_per_s = w.batch / (ms_per_step * 1e-3)
+    bytes_launch = algorithmic_bytes(w) * w.batch
+    flops_launch = algorithmic_flops(w) * w.batch
+    achieved_gbs = bytes_launch / (kernel_ms * 1e-3) / 1e9
+    gflops = flops_launch / (ms_per_step * 1e-3) / 1e9
+    kind = "register"
+    line = {
+        "metric": METRIC,
+        "value": mats_per_s,
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"float32": "f32", "float64": "f64", "complex64": "c64", "complex128": "c128"}[np.dtype(w.dtype).name],
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": w.op, "n": w.n, "nrhs": w.nrhs, "batch": w.batch,
+                   "tier": lib.TIER_NAMES.get(tier, str(tier))},
+        "gflops": gflops,
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profile(w.name, kind),
+                     "kernel_ms": kernel_ms, "algorithmic_bytes_per_launch": bytes_launch},
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

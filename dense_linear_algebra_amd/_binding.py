@@ -1,0 +1,126 @@
+"""ctypes binding of libbatchlu.so: the C ABI under the same names.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+library; a missing library is an error, never a fallback.  Pointer arguments
+accept a torch tensor (its data_ptr is passed), a plain int (a device
+address) or None (NULL).  ``stream`` accepts a torch.cuda.Stream, an int
+handle or None (torch's current stream when torch is initialised on a GPU,
+else the null stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbatchlu.so")
+
+R32, R64, C64, C128 = 0, 1, 2, 3
+TIER_AUTO, TIER_TINY, TIER_CTA, TIER_BLOCKED = 0, 1, 2, 3
+TIER_NAMES = {TIER_TINY: "tiny", TIER_CTA: "cta", TIER_BLOCKED: "blocked"}
+OK, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_LAUNCH = 0, -100, -101, -102
+
+_lib = None
+
+
+class BatchLUError(RuntimeError):
+    def __init__(self, func, status):
+        self.status = status
+        super().__init__(f"{func} returned {status}: {status_string(status)}")
+
+
+def load():
+    """Load libbatchlu.so (built by ``python -m dense_linear_algebra_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m dense_linear_algebra_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, ch = ctypes.c_int, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_char
+    lib.batchlu_getrf.argtypes = [i32, i32, vp, i32, i64, vp, i64, vp, i32, vp]
+    lib.batchlu_getrs.argtypes = [i32, ch, i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, i32, vp]
+    lib.batchlu_gesv.argtypes = [i32, i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, vp, i32, vp]
+    lib.batchlu_select_tier.argtypes = [i32, i32, i32, i32, i32]
+    lib.batchlu_set_tier.argtypes = [i32]
+    lib.batchlu_status_string.argtypes = [i32]
+    lib.batchlu_status_string.restype = ctypes.c_char_p
+    lib.batchlu_version.argtypes = []
+    lib.batchlu_version.restype = ctypes.c_char_p
+    for f in ("batchlu_getrf", "batchlu_getrs", "batchlu_gesv", "batchlu_select_tier", "batchlu_set_tier"):
+        getattr(lib, f).restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        try:
+            import torch
+            if torch.cuda.is_available() and torch.cuda.is_initialized():
+                return torch.cuda.current_stream().cuda_stream
+        except Exception:
+            pass
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def dtype_code(dtype) -> int:
+    """Library code of a torch or numpy dtype."""
+    name = str(dtype).replace("torch.", "")
+    codes = {"float32": R32, "float64": R64, "complex64": C64, "complex128": C128}
+    if name not in codes:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return codes[name]
+
+
+def _check(func, status, raise_on_error):
+    if raise_on_error and status != OK:
+        raise BatchLUError(func, status)
+    return status
+
+
+def batchlu_getrf(t, n, A, lda, strideA, ipiv, strideP, info, batch, stream=None, raise_on_error=True):
+    st = load().batchlu_getrf(t, n, _ptr(A), lda, strideA, _ptr(ipiv), strideP, _ptr(info), batch, _stream(stream))
+    return _check("batchlu_getrf", st, raise_on_error)
+
+
+def batchlu_getrs(t, trans, n, nrhs, A, lda, strideA, ipiv, strideP, B, ldb, strideB, batch, stream=None,
+                  raise_on_error=True):
+    tr = trans.encode() if isinstance(trans, str) else bytes([trans])
+    st = load().batchlu_getrs(t, tr, n, nrhs, _ptr(A), lda, strideA, _ptr(ipiv), strideP, _ptr(B), ldb, strideB,
+                              batch, _stream(stream))
+    return _check("batchlu_getrs", st, raise_on_error)
+
+
+def batchlu_gesv(t, n, nrhs, A, lda, strideA, ipiv, strideP, B, ldb, strideB, info, batch, stream=None,
+                 raise_on_error=True):
+    st = load().batchlu_gesv(t, n, nrhs, _ptr(A), lda, strideA, _ptr(ipiv), strideP, _ptr(B), ldb, strideB,
+                             _ptr(info), batch, _stream(stream))
+    return _check("batchlu_gesv", st, raise_on_error)
+
+
+def batchlu_select_tier(t, op, n, nrhs, batch):
+    return load().batchlu_select_tier(t, op, n, nrhs, batch)
+
+
+def batchlu_set_tier(tier):
+    return load().batchlu_set_tier(tier)
+
+
+def status_string(status):
+    return load().batchlu_status_string(status).decode()
+
+
+def version():
+    return load().batchlu_version().decode()

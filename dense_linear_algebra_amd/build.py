@@ -1,0 +1,73 @@
+"""Build libbatchlu.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+    python -m dense_linear_algebra_amd.build [-v]
+
+Every HIP source is compiled with IEEE semantics: -ffp-contract=off (no fused
+multiply-add except the ones the code spells), no fast-math, and without the
+packed-FP32 VALU forms.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libbatchlu.so")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+          "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-pragma-unroll-threshold=2000000"]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def _compile(src: str, verbose: bool, extra=()):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC, "-c", src, "-o", obj] + COMMON + list(extra)
+    if src.endswith(".hip"):
+        cmd += DEVICE
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    with open(obj + ".log", "w") as f:
+        f.write(r.stderr)
+    if verbose and r.stderr.strip():
+        print(r.stderr, flush=True)
+    return obj, r.stderr
+
+
+def build_library(verbose: bool = False, jobs: int | None = None, extra=()) -> str:
+    """Compile every source (in parallel) and link libbatchlu.so; always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = [o for o, _ in ex.map(lambda s: _compile(s, verbose, extra), srcs)]
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    v = "-v" in sys.argv
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if "--resources" in sys.argv else []
+    print(build_library(verbose=v, extra=extra))

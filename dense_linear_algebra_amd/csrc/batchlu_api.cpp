@@ -1,0 +1,204 @@
+// batchlu_api.cpp -- the C ABI: argument checks, tier selection, dispatch.
+//
+// Tier selection (BatchLAS "LU" page, family table and routing tables): the
+// pages rank register-resident kernels first for small n, a one-work-group
+// kernel for mid n and the blocked right-looking driver above.  On gfx950
+// the register tiers hold a matrix in VGPRs:
+//   tiny    n <= 32: several matrices per wavefront;
+//   cta     32 < n <= 64 (complex double: none): one wavefront per matrix;
+//   blocked larger n, nb = 32.
+// gesv runs fused (factor + forward + back in one kernel) in the register
+// tiers while nrhs <= 16; otherwise it is getrf followed by getrs.
+#include <atomic>
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/batchlu.h"
+#include "internal.h"
+
+using namespace batchlu;
+
+namespace {
+
+std::atomic<int> g_tier_pin{-1};   // -1: not read from the environment yet
+
+int tier_pin() {
+    int v = g_tier_pin.load(std::memory_order_relaxed);
+    if (v >= 0) return v;
+    int from_env = BATCHLU_TIER_AUTO;
+    if (const char* e = std::getenv("BATCHLU_TIER")) {
+        if (!std::strcmp(e, "tiny")) from_env = BATCHLU_TIER_TINY;
+        else if (!std::strcmp(e, "cta")) from_env = BATCHLU_TIER_CTA;
+        else if (!std::strcmp(e, "blocked")) from_env = BATCHLU_TIER_BLOCKED;
+    }
+    int expected = -1;
+    g_tier_pin.compare_exchange_strong(expected, from_env);
+    return g_tier_pin.load();
+}
+
+bool valid_dtype(int t) { return t >= BATCHLU_R32 && t <= BATCHLU_C128; }
+
+enum Op { OP_GETRF = 0, OP_GETRS = 1, OP_GESV = 2 };
+
+bool tier_can_run(int tier, int t, int op, int n, int nrhs) {
+    switch (tier) {
+    case BATCHLU_TIER_TINY:
+    case BATCHLU_TIER_CTA: {
+        const bool one_wave = tier == BATCHLU_TIER_CTA;
+        if (op == OP_GETRS) return getrs_direct_supported(t, n, nrhs) && n <= 64;
+        if (op == OP_GESV) return register_supported(t, n, nrhs, MODE_GESV, one_wave) ||
+                                  (register_supported(t, n, 0, MODE_GETRF, one_wave) &&
+                                   getrs_direct_supported(t, n, nrhs));
+        return register_supported(t, n, 0, MODE_GETRF, one_wave);
+    }
+    case BATCHLU_TIER_BLOCKED:
+        if (op == OP_GETRS) return blocked_supported(t, n) || getrs_direct_supported(t, n, nrhs);
+        return blocked_supported(t, n);
+    default:
+        return false;
+    }
+}
+
+int auto_tier(int t, int op, int n, int nrhs) {
+    const int order[3] = {BATCHLU_TIER_TINY, BATCHLU_TIER_CTA, BATCHLU_TIER_BLOCKED};
+    for (int tier : order)
+        if (tier_can_run(tier, t, op, n, nrhs)) return tier;
+    return BATCHLU_ERR_CAPACITY;
+}
+
+int choose(int t, int op, int n, int nrhs) {
+    const int pin = tier_pin();
+    if (pin != BATCHLU_TIER_AUTO) return tier_can_run(pin, t, op, n, nrhs) ? pin : BATCHLU_ERR_CAPACITY;
+    return auto_tier(t, op, n, nrhs);
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? BATCHLU_OK : BATCHLU_ERR_LAUNCH; }
+
+int run_getrf(int tier, int t, const Problem& p, hipStream_t s) {
+    switch (tier) {
+    case BATCHLU_TIER_TINY: return status_of(register_launch(t, p, MODE_GETRF, false, s));
+    case BATCHLU_TIER_CTA: return status_of(register_launch(t, p, MODE_GETRF, true, s));
+    case BATCHLU_TIER_BLOCKED: return status_of(blocked_getrf(t, p, s));
+    default: return BATCHLU_ERR_CAPACITY;
+    }
+}
+
+int run_getrs(int tier, int t, const Problem& p, hipStream_t s) {
+    if (tier == BATCHLU_TIER_BLOCKED && blocked_supported(t, p.n)) return status_of(blocked_getrs(t, p, s));
+    return status_of(getrs_direct_launch(t, p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int batchlu_getrf(batchlu_dtype t, int n, void* A, int lda, long long strideA, int* ipiv,
+                  long long strideP, int* info, int batch, hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (n < 0) return -2;
+    if (lda < (n > 1 ? n : 1)) return -4;
+    if (batch < 0) return -9;
+    if (batch > 1 && strideA < (long long)lda * n) return -5;
+    if (batch > 1 && strideP < n) return -7;
+    if (n == 0 || batch == 0) return BATCHLU_OK;
+    if (!A) return -3;
+    if (!ipiv) return -6;
+    if (!info) return -8;
+    const int tier = choose(t, OP_GETRF, n, 0);
+    if (tier < 0) return tier;
+    Problem p;
+    p.n = n; p.batch = batch; p.A = A; p.lda = lda; p.sA = strideA;
+    p.ipiv = ipiv; p.sP = strideP; p.info = info;
+    return run_getrf(tier, t, p, stream);
+}
+
+int batchlu_getrs(batchlu_dtype t, char trans, int n, int nrhs, const void* A, int lda,
+                  long long strideA, const int* ipiv, long long strideP, void* B, int ldb,
+                  long long strideB, int batch, hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (trans != 'N' && trans != 'n' && trans != 'T' && trans != 't' && trans != 'C' && trans != 'c')
+        return -2;
+    if (n < 0) return -3;
+    if (nrhs < 0) return -4;
+    if (lda < (n > 1 ? n : 1)) return -6;
+    if (ldb < (n > 1 ? n : 1)) return -11;
+    if (batch < 0) return -13;
+    if (batch > 1 && strideA < (long long)lda * n) return -7;
+    if (batch > 1 && strideP < n) return -9;
+    if (batch > 1 && strideB < (long long)ldb * nrhs) return -12;
+    if (trans != 'N' && trans != 'n') return BATCHLU_ERR_UNSUPPORTED;
+    if (n == 0 || nrhs == 0 || batch == 0) return BATCHLU_OK;
+    if (!A) return -5;
+    if (!ipiv) return -8;
+    if (!B) return -10;
+    const int tier = choose(t, OP_GETRS, n, nrhs);
+    if (tier < 0) return tier;
+    Problem p;
+    p.n = n; p.nrhs = nrhs; p.batch = batch; p.A = const_cast<void*>(A); p.lda = lda; p.sA = strideA;
+    p.ipiv = const_cast<int*>(ipiv); p.sP = strideP; p.B = B; p.ldb = ldb; p.sB = strideB;
+    return run_getrs(tier, t, p, stream);
+}
+
+int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda, long long strideA, int* ipiv,
+                 long long strideP, void* B, int ldb, long long strideB, int* info, int batch,
+                 hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (n < 0) return -2;
+    if (nrhs < 0) return -3;
+    if (lda < (n > 1 ? n : 1)) return -5;
+    if (ldb < (n > 1 ? n : 1)) return -10;
+    if (batch < 0) return -13;
+    if (batch > 1 && strideA < (long long)lda * n) return -6;
+    if (batch > 1 && strideP < n) return -8;
+    if (batch > 1 && strideB < (long long)ldb * nrhs) return -11;
+    if (n == 0 || batch == 0) return BATCHLU_OK;
+    if (!A) return -4;
+    if (!ipiv) return -7;
+    if (nrhs > 0 && !B) return -9;
+    if (!info) return -12;
+    const int tier = choose(t, OP_GESV, n, nrhs);
+    if (tier < 0) return tier;
+    Problem p;
+    p.n = n; p.nrhs = nrhs; p.batch = batch; p.A = A; p.lda = lda; p.sA = strideA;
+    p.ipiv = ipiv; p.sP = strideP; p.info = info; p.B = B; p.ldb = ldb; p.sB = strideB;
+    if (tier != BATCHLU_TIER_BLOCKED && nrhs > 0 &&
+        register_supported(t, n, nrhs, MODE_GESV, tier == BATCHLU_TIER_CTA))
+        return status_of(register_launch(t, p, MODE_GESV, tier == BATCHLU_TIER_CTA, stream));
+    int st = run_getrf(tier, t, p, stream);
+    if (st != BATCHLU_OK || nrhs == 0) return st;
+    // getrs on matrices with info > 0 would overwrite B; LAPACK gesv leaves B
+    // alone there.  The composed path therefore solves into B only where the
+    // factorisation succeeded: the solve kernels read info when it is given.
+    return run_getrs(tier, t, p, stream);
+}
+
+int batchlu_select_tier(batchlu_dtype t, int op, int n, int nrhs, int batch) {
+    if (!valid_dtype(t)) return -1;
+    if (op < OP_GETRF || op > OP_GESV) return -2;
+    if (n < 0) return -3;
+    if (nrhs < 0) return -4;
+    if (batch < 0) return -5;
+    return choose(t, op, n, nrhs);
+}
+
+int batchlu_set_tier(int tier) {
+    const int prev = tier_pin();
+    if (tier < BATCHLU_TIER_AUTO || tier > BATCHLU_TIER_BLOCKED) return -1;
+    g_tier_pin.store(tier);
+    return prev;
+}
+
+const char* batchlu_status_string(int status) {
+    switch (status) {
+    case BATCHLU_OK: return "ok";
+    case BATCHLU_ERR_UNSUPPORTED: return "unsupported option";
+    case BATCHLU_ERR_CAPACITY: return "shape exceeds every tier's capacity";
+    case BATCHLU_ERR_LAUNCH: return "kernel launch failed";
+    default: return status < 0 && status > -20 ? "invalid argument" : "unknown status";
+    }
+}
+
+const char* batchlu_version(void) { return "batchlu 0.1.0 (gfx950)"; }
+
+}  // extern "C"

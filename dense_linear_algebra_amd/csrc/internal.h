@@ -1,0 +1,39 @@
+// internal.h -- host-side interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace batchlu {
+
+enum Dtype { R32 = 0, R64 = 1, C64 = 2, C128 = 3 };
+
+inline int elem_bytes(int t) { return t == R32 ? 4 : (t == C128 ? 16 : 8); }
+
+// One batched problem on strided, column-major storage.  Offsets are in
+// elements of the data type.  `mode` selects what a fused kernel does.
+struct Problem {
+    int n = 0, nrhs = 0, batch = 0;
+    void* A = nullptr;  int lda = 0;  long long sA = 0;
+    int* ipiv = nullptr;  long long sP = 0;
+    int* info = nullptr;
+    void* B = nullptr;  int ldb = 0;  long long sB = 0;
+};
+
+enum Mode { MODE_GETRF = 0, MODE_GESV = 1 };
+
+// Register tiers.  Return hipSuccess, or the launch error.  `supported`
+// answers whether the kernel set holds an instantiation for the shape.
+bool register_supported(int dtype, int n, int nrhs, int mode, bool one_wave_per_matrix);
+hipError_t register_launch(int dtype, const Problem& p, int mode, bool one_wave_per_matrix,
+                           hipStream_t s);
+
+// Solve with given factors, any n (one work-group per matrix and RHS tile).
+bool getrs_direct_supported(int dtype, int n, int nrhs);
+hipError_t getrs_direct_launch(int dtype, const Problem& p, hipStream_t s);
+
+// Blocked right-looking tier (panel, laswp, trsm, gemm) and blocked getrs.
+bool blocked_supported(int dtype, int n);
+hipError_t blocked_getrf(int dtype, const Problem& p, hipStream_t s);
+hipError_t blocked_getrs(int dtype, const Problem& p, hipStream_t s);
+
+}  // namespace batchlu

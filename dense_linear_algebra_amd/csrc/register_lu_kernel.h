@@ -1,0 +1,453 @@
+// register_lu_kernel.h -- register-resident LU with partial pivoting, and the
+// fused factor-and-solve, for small matrices (n <= 64) on gfx950.
+//
+// Design (BatchLAS "LU" page, tiny-tier paragraph and the gesv-tiny
+// paragraph; redesigned for wave64):
+//   - A matrix lives in a group of LPM lanes of one wavefront; each lane owns
+//     RPL consecutive rows (row = RPL*lane_in_group + slot) of A and of B in
+//     VGPRs.  64 / LPM matrices share a wavefront.  Rows and columns past n
+//     carry the identity, so the unrolled body needs no per-row guards.
+//   - Row interchanges are lazy: each slot carries its current position
+//     `pos`; a step relabels two positions and moves no data.
+//   - Pivot search: per-slot keys (metric bits + 1, NaN mapped) reduced with
+//     DPP / ds_swizzle inside the group; ties go to the lowest position by a
+//     second min-reduction over positions.
+//   - The pivot row is published through a per-group LDS row (one lane
+//     writes, the group reads it back as a broadcast).  All lanes of a group
+//     are in one wavefront and LDS operations of a wavefront complete in
+//     order, so no barrier is needed.
+//   - For gesv the right-hand sides ride along as extra columns of the rank-1
+//     update (the forward solve).  The back substitution multiplies by the
+//     reciprocal of each diagonal entry, computed once at its elimination
+//     step (BatchLAS "Blackwell" page, getrs tiny paragraph); X is staged in
+//     LDS and stored with row-contiguous vector writes.
+// Arithmetic per element is the same operation sequence as the unblocked
+// right-looking LU, so L, U and ipiv are bit-identical to it.
+#pragma once
+
+#include <stdlib.h>
+
+#include "device_ops.h"
+#include "internal.h"
+
+namespace batchlu {
+
+namespace reg_detail {
+
+constexpr int kWavesPerBlock = 4;
+
+template <int BYTES>
+struct vecbits;
+template <>
+struct vecbits<4> { using type = uint32_t; };
+template <>
+struct vecbits<8> { using type = uint2; };
+template <>
+struct vecbits<16> { using type = uint4; };
+
+template <typename T, int NB, int RPL, int NR>
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+register_lu_kernel(Problem p, int mode)
+{
+    using O = ops<T>;
+    using R = typename O::R;
+    using K = typename O::K;
+    constexpr int LPM = NB / RPL;                  // lanes per matrix
+    constexpr int GPW = 64 / LPM;                  // matrices per wavefront
+    constexpr int GPB = GPW * kWavesPerBlock;      // matrices per block
+    constexpr int CH = 16 / (int)sizeof(T);        // elements per 16-byte chunk
+    constexpr int NBC = NB / CH;                   // chunks of an A row
+    constexpr int NRC = (NR + CH - 1) / CH;        // chunks of a B row
+    constexpr int NRP = NRC * CH > 0 ? NRC * CH : 1;
+    constexpr int ROWC = NBC + NRC;
+    constexpr int NPIV = (NB + LPM - 1) / LPM;     // pivots recorded per lane
+    constexpr int XC = NR > 0 ? NB * NRC : 1;      // chunks of the staged X
+    constexpr int DGC = NR > 0 ? (2 * NB + CH - 1) / CH : 1;   // chunks of (1/u_jj, u_jj)
+    constexpr int VB = RPL * (int)sizeof(T);       // bytes of a lane's rows in one column
+    static_assert(NB % CH == 0 && NB % RPL == 0 && LPM <= 64 && 64 % LPM == 0, "bad shape");
+
+    __shared__ uint4 rowbuf[GPB][ROWC];
+    __shared__ uint4 xstage[GPB][XC];   // X row k at chunks [k*NRC, (k+1)*NRC)
+    __shared__ uint4 diagbuf[GPB][DGC]; // (1/u_jj, u_jj) of every step j
+
+    const int lane = threadIdx.x & 63;
+    const int grp = (threadIdx.x >> 6) * GPW + lane / LPM;
+    const int li = lane % LPM;
+    const int n = p.n;
+
+    long long m = (long long)blockIdx.x * GPB + grp;
+    const bool live = m < p.batch;
+    if (!live) m = p.batch - 1;   // idle groups factor a copy and store nothing
+
+    T* A = (T*)p.A + m * p.sA;
+    T* B = (T*)p.B + m * p.sB;
+    const bool solve = (NR > 0) && mode == MODE_GESV;
+    T* diag = (T*)&diagbuf[grp][0];
+
+    T a[RPL][NB];
+    T b[RPL][NRP];
+    int pos[RPL];
+
+    // ---- load (identity padding past n) ----------------------------------
+    const bool full = (n == NB) && (VB <= 16) && ((p.lda * sizeof(T)) % VB == 0) &&
+                      (((uintptr_t)A) % VB == 0);
+#pragma unroll
+    for (int s = 0; s < RPL; ++s) pos[s] = li * RPL + s;
+    if constexpr (VB <= 16) {
+        using V = typename vecbits<VB>::type;
+        if (full) {
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                V w = *(const V*)(A + li * RPL + (long long)k * p.lda);
+                T tmp[RPL];
+                __builtin_memcpy(tmp, &w, sizeof(tmp));
+#pragma unroll
+                for (int s = 0; s < RPL; ++s) a[s][k] = tmp[s];
+            }
+        }
+    }
+    if (!full) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+#pragma unroll
+            for (int s = 0; s < RPL; ++s) {
+                const int row = li * RPL + s;
+                T v = (row == k) ? O::one() : O::zero();
+                if (k < n && row < n) v = A[row + (long long)k * p.lda];
+                a[s][k] = v;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NRP; ++r) {
+#pragma unroll
+        for (int s = 0; s < RPL; ++s) {
+            const int row = li * RPL + s;
+            T v = O::zero();
+            if (solve && r < NR && r < p.nrhs && row < n) v = B[row + (long long)r * p.ldb];
+            b[s][r] = v;
+        }
+    }
+
+    // ---- elimination -------------------------------------------------------
+    int info = 0;
+    int pivrec[NPIV];
+#pragma unroll
+    for (int t = 0; t < NPIV; ++t) pivrec[t] = 0;
+
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        if (j >= n) continue;   // uniform; keeps the trip count constant for full unrolling
+
+        // a1: argmax of the metric over rows at positions >= j
+        K key[RPL];
+        K kmax = 0;
+#pragma unroll
+        for (int s = 0; s < RPL; ++s) {
+            K kk = (pos[s] >= j) ? (K)pivot_key(O::metric(a[s][j])) : (K)0;
+            key[s] = kk;
+            kmax = kk > kmax ? kk : kmax;
+        }
+        kmax = group_max<LPM>(kmax);
+        int q = 0x7fffffff;
+#pragma unroll
+        for (int s = 0; s < RPL; ++s)
+            if (key[s] == kmax && pos[s] < q) q = pos[s];
+        const int piv_pos = group_min<LPM>(q);
+        if (li == j % LPM) pivrec[j / LPM] = piv_pos;
+
+        // publish the pivot row (chunks from the one holding column j)
+#pragma unroll
+        for (int s = 0; s < RPL; ++s) {
+            if (pos[s] == piv_pos) {
+#pragma unroll
+                for (int c = 0; c < NBC; ++c) {
+                    if (c < j / CH) continue;
+                    uint4 w;
+                    __builtin_memcpy(&w, &a[s][c * CH], 16);
+                    rowbuf[grp][c] = w;
+                }
+                if constexpr (NRC > 0) {
+                    if (solve) {
+#pragma unroll
+                        for (int c = 0; c < NRC; ++c) {
+                            uint4 w;
+                            __builtin_memcpy(&w, &b[s][c * CH], 16);
+                            rowbuf[grp][NBC + c] = w;
+                        }
+                    }
+                }
+            }
+        }
+        // a2: lazy interchange of positions j and piv_pos
+#pragma unroll
+        for (int s = 0; s < RPL; ++s)
+            pos[s] = (pos[s] == piv_pos) ? j : (pos[s] == j ? piv_pos : pos[s]);
+
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        T u[NB];
+        T ub[NRP];
+#pragma unroll
+        for (int c = 0; c < NBC; ++c) {
+            if (c < j / CH) continue;
+            uint4 w = rowbuf[grp][c];
+            __builtin_memcpy(&u[c * CH], &w, 16);
+        }
+        if constexpr (NRC > 0) {
+            if (solve) {
+#pragma unroll
+                for (int c = 0; c < NRC; ++c) {
+                    uint4 w = rowbuf[grp][NBC + c];
+                    __builtin_memcpy(&ub[c * CH], &w, 16);
+                }
+            }
+        }
+
+        const T piv = u[j];
+        const R pm = O::metric(piv);
+        const bool zero = (pm == R(0));
+        if (zero && info == 0) info = j + 1;
+        const T r = O::recip(piv);
+        const bool small = !(pm >= O::sfmin());
+        if constexpr (NR > 0) {
+            if (solve && li == 0) {
+                diag[2 * j] = r;
+                diag[2 * j + 1] = piv;
+            }
+        }
+
+        // a3: multipliers l = a * r; a pivot below the smallest normal takes
+        // l = a / pivot instead.  That path is rare and sits behind a
+        // wavefront-uniform branch (the empty asm keeps the compiler from
+        // executing the divisions speculatively on every step).
+        T lm[RPL];
+#pragma unroll
+        for (int s = 0; s < RPL; ++s) lm[s] = O::mul(a[s][j], r);
+        if (__builtin_amdgcn_ballot_w64(small) != 0) {
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int s = 0; s < RPL; ++s)
+                if (small) lm[s] = O::div(a[s][j], piv);
+        }
+
+        // a4: rank-1 update of the rows below position j
+#pragma unroll
+        for (int s = 0; s < RPL; ++s) {
+            if (pos[s] > j && !zero) {
+                const T l = lm[s];
+                a[s][j] = l;
+#pragma unroll
+                for (int k = 0; k < NB; ++k)
+                    if (k > j) O::fms(a[s][k], l, u[k]);
+                if constexpr (NR > 0) {
+                    if (solve) {
+#pragma unroll
+                        for (int r2 = 0; r2 < NR; ++r2) O::fms(b[s][r2], l, ub[r2]);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- back substitution U x = y (gesv) ---------------------------------
+    // Step k: the row at position k publishes y_k, every lane forms
+    // x_k = y_k * (1/u_kk) (or y_k / u_kk when u_kk is below the smallest
+    // normal), lane 0 of the group stages x_k, and the rows above position k
+    // subtract u_ik * x_k.
+    if constexpr (NR > 0) {
+        if (solve) {
+#pragma unroll
+            for (int k = NB - 1; k >= 0; --k) {
+                if (k >= n) continue;
+#pragma unroll
+                for (int s = 0; s < RPL; ++s) {
+                    if (pos[s] == k) {
+#pragma unroll
+                        for (int c = 0; c < NRC; ++c) {
+                            uint4 w;
+                            __builtin_memcpy(&w, &b[s][c * CH], 16);
+                            rowbuf[grp][c] = w;
+                        }
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                T xk[NRP];
+#pragma unroll
+                for (int c = 0; c < NRC; ++c) {
+                    uint4 w = rowbuf[grp][c];
+                    __builtin_memcpy(&xk[c * CH], &w, 16);
+                }
+                const T rk = diag[2 * k];
+                const T dk = diag[2 * k + 1];
+                const bool tiny = !(O::metric(dk) >= O::sfmin());
+                if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int r2 = 0; r2 < NR; ++r2) xk[r2] = tiny ? O::div(xk[r2], dk) : O::mul(xk[r2], rk);
+                } else {
+#pragma unroll
+                    for (int r2 = 0; r2 < NR; ++r2) xk[r2] = O::mul(xk[r2], rk);
+                }
+                if (li == 0) {
+#pragma unroll
+                    for (int c = 0; c < NRC; ++c) {
+                        uint4 w;
+                        __builtin_memcpy(&w, &xk[c * CH], 16);
+                        xstage[grp][k * NRC + c] = w;
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < RPL; ++s) {
+                    if (pos[s] < k) {
+#pragma unroll
+                        for (int r2 = 0; r2 < NR; ++r2) O::fms(b[s][r2], a[s][k], xk[r2]);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
+    }
+
+    // ---- store -------------------------------------------------------------
+    if (!live) return;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        if (k >= n) continue;
+#pragma unroll
+        for (int s = 0; s < RPL; ++s)
+            if (pos[s] < n) A[pos[s] + (long long)k * p.lda] = a[s][k];
+    }
+    int* ipiv = p.ipiv + m * p.sP;
+#pragma unroll
+    for (int t = 0; t < NPIV; ++t) {
+        const int j = t * LPM + li;
+        if (j < n) ipiv[j] = pivrec[t] + 1;
+    }
+    if (li == 0) p.info[m] = info;
+    if constexpr (NR > 0) {
+        if (solve && info == 0) {
+            // X rows li*RPL .. li*RPL+RPL-1 from the stage
+            T xr[RPL][NRP];
+#pragma unroll
+            for (int s = 0; s < RPL; ++s) {
+                const int row = li * RPL + s;
+#pragma unroll
+                for (int c = 0; c < NRC; ++c) {
+                    uint4 w = xstage[grp][row * NRC + c];
+                    __builtin_memcpy(&xr[s][c * CH], &w, 16);
+                }
+            }
+            const bool bfull = (n == NB) && (VB <= 16) && ((p.ldb * sizeof(T)) % VB == 0) &&
+                               (((uintptr_t)B) % VB == 0);
+#pragma unroll
+            for (int r2 = 0; r2 < NR; ++r2) {
+                if (r2 >= p.nrhs) continue;
+                bool done = false;
+                if constexpr (VB <= 16) {
+                    using V = typename vecbits<VB>::type;
+                    if (bfull) {
+                        T tmp[RPL];
+#pragma unroll
+                        for (int s = 0; s < RPL; ++s) tmp[s] = xr[s][r2];
+                        V w;
+                        __builtin_memcpy(&w, tmp, sizeof(tmp));
+                        *(V*)(B + li * RPL + (long long)r2 * p.ldb) = w;
+                        done = true;
+                    }
+                }
+                if (!done) {
+#pragma unroll
+                    for (int s = 0; s < RPL; ++s) {
+                        const int row = li * RPL + s;
+                        if (row < n) B[row + (long long)r2 * p.ldb] = xr[s][r2];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// instantiation table
+// ---------------------------------------------------------------------------
+struct Shape {
+    int nb, rpl;
+};
+
+// Partition per data type and row bucket: lanes per matrix = nb / rpl.
+// Several matrices per wavefront ("tiny") up to n = 32; one wavefront per
+// matrix for n in (32, 64] ("cta").
+inline Shape pick_shape(int dtype, int n) {
+    int nb = n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : n <= 32 ? 32 : 64;
+    int rpl;
+    switch (dtype) {
+    case R32: rpl = nb <= 8 ? 4 : nb <= 32 ? 2 : 1; break;
+    case R64: rpl = nb <= 16 ? 2 : 1; break;
+    case C64: rpl = nb <= 16 ? 2 : 1; break;
+    default: rpl = 1; break;
+    }
+    return Shape{nb, rpl};
+}
+
+inline int pick_nr(int nrhs, int mode) {
+    if (mode != MODE_GESV) return 0;
+    return nrhs <= 1 ? 1 : nrhs <= 8 ? 8 : nrhs <= 16 ? 16 : -1;
+}
+
+template <typename T, int NB, int RPL, int NR>
+hipError_t launch_one(const Problem& p, int mode, hipStream_t s) {
+    constexpr int LPM = NB / RPL;
+    constexpr int GPB = (64 / LPM) * kWavesPerBlock;
+    const long long blocks = (p.batch + GPB - 1) / GPB;
+    hipLaunchKernelGGL((register_lu_kernel<T, NB, RPL, NR>), dim3((unsigned)blocks),
+                       dim3(64 * kWavesPerBlock), 0, s, p, mode);
+    return hipGetLastError();
+}
+
+template <typename T, int NB, int RPL>
+hipError_t launch_nr(const Problem& p, int mode, int nr, hipStream_t s) {
+    switch (nr) {
+    case 0: return launch_one<T, NB, RPL, 0>(p, mode, s);
+    case 1: return launch_one<T, NB, RPL, 1>(p, mode, s);
+    case 8: return launch_one<T, NB, RPL, 8>(p, mode, s);
+    case 16: return launch_one<T, NB, RPL, 16>(p, mode, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_type(const Problem& p, int mode, hipStream_t s) {
+    constexpr int dtype = sizeof(T) == 4 ? R32 : sizeof(T) == 16 ? C128 : (ops<T>::is_complex ? C64 : R64);
+    Shape sh = pick_shape(dtype, p.n);
+    const int nr = pick_nr(p.nrhs, mode);
+    constexpr bool big = sizeof(T) == 16;
+#define BATCHLU_CASE(NBV, RPLV)                                                  \
+    if (sh.nb == NBV && sh.rpl == RPLV) return launch_nr<T, NBV, RPLV>(p, mode, nr, s);
+    if constexpr (sizeof(T) == 4) {
+        if (const char* e = getenv("BATCHLU_TINY_RPL")) {   // A/B timing of the partition
+            const int v = atoi(e);
+            if (sh.nb >= 16 && sh.nb <= 32 && (v == 1 || v == 2 || v == 4)) sh.rpl = v;
+        }
+        BATCHLU_CASE(4, 4) BATCHLU_CASE(8, 4) BATCHLU_CASE(16, 4) BATCHLU_CASE(32, 4)
+        BATCHLU_CASE(16, 2) BATCHLU_CASE(32, 2) BATCHLU_CASE(16, 1) BATCHLU_CASE(32, 1)
+        BATCHLU_CASE(64, 1)
+    } else if constexpr (!big) {
+        BATCHLU_CASE(4, 2) BATCHLU_CASE(8, 2) BATCHLU_CASE(16, 2) BATCHLU_CASE(32, 1)
+        BATCHLU_CASE(64, 1)
+    } else {
+        BATCHLU_CASE(4, 1) BATCHLU_CASE(8, 1) BATCHLU_CASE(16, 1) BATCHLU_CASE(32, 1)
+    }
+#undef BATCHLU_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace reg_detail
+
+}  // namespace batchlu

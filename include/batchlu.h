@@ -1,0 +1,138 @@
+/*
+ * batchlu.h -- C ABI of the batched LU library for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (BatchLAS performance notes, "LU" page, family table at the top
+ * of the page): getrf factors each matrix of a homogeneous batch with partial
+ * pivoting, P*A = L*U; getrs solves A*X = B from those factors; gesv is the
+ * composition of the two.
+ *
+ * Common conventions (same page: the tiny-tier and register-panel paragraphs
+ * fix ipiv and info; the common can_run term fixes square A and B.rows == n;
+ * the Blackwell page's trsm paragraph requires padded leading dimensions and
+ * batch strides to work):
+ *   - Every matrix is column-major.  Element (i, j) of matrix b of A is at
+ *     A + b*strideA + i + j*lda, counted in elements of the data type.
+ *     Complex types are interleaved (re, im) pairs, like std::complex.
+ *   - All pointers are DEVICE pointers and stay owned by the caller.  The
+ *     library allocates nothing per call and frees nothing.
+ *   - Every call is asynchronous on `stream` (0 = the null stream).  ipiv,
+ *     info, the factors and X are valid once the stream has reached the
+ *     point after the call.
+ *   - ipiv is int32, 1-based and global: ipiv[b*strideP + j] = p + 1 means
+ *     rows j and p were exchanged at step j (in that order, j = 0 .. n-1).
+ *   - info[b] = 0 on success, or j + 1 for the first step j whose pivot is
+ *     exactly zero.  The factorisation still completes (the zero column is
+ *     left unscaled).  A numerically singular matrix is not an error.
+ *   - Pivot choice: the largest |a| (real) or |re| + |im| (complex) in the
+ *     column; ties go to the lowest row; a NaN ranks above every number and
+ *     the first NaN wins.
+ *   - Arguments are checked on the host before anything is launched.  A bad
+ *     argument returns -k, where k is its 1-based position in the signature.
+ *     n == 0, nrhs == 0 or batch == 0 succeed without launching anything.
+ *   - A shape no tier can run is refused with BATCHLU_ERR_CAPACITY, never
+ *     truncated (BatchLAS "trsm" page: the over-capacity defect).
+ */
+#ifndef BATCHLU_H
+#define BATCHLU_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BATCHLU_R32 = 0,   /* float                    */
+    BATCHLU_R64 = 1,   /* double                   */
+    BATCHLU_C64 = 2,   /* complex float  (re, im)  */
+    BATCHLU_C128 = 3   /* complex double (re, im)  */
+} batchlu_dtype;
+
+/* status codes (negative values -1 .. -20 name an invalid argument) */
+#define BATCHLU_OK 0
+#define BATCHLU_ERR_UNSUPPORTED (-100) /* e.g. trans other than 'N'            */
+#define BATCHLU_ERR_CAPACITY (-101)    /* no tier can run this shape           */
+#define BATCHLU_ERR_LAUNCH (-102)      /* a kernel launch failed (HIP error)   */
+
+/* tiers (see batchlu_select_tier) */
+#define BATCHLU_TIER_AUTO 0
+#define BATCHLU_TIER_TINY 1    /* several matrices per wavefront, rows in VGPRs */
+#define BATCHLU_TIER_CTA 2     /* one work-group per matrix, rows in VGPRs       */
+#define BATCHLU_TIER_BLOCKED 3 /* nb = 32 right-looking: panel, laswp, trsm, gemm */
+
+/*
+ * batchlu_getrf -- LU with partial pivoting of `batch` n x n matrices, in place.
+ *   1 t        data type
+ *   2 n        order, n >= 0
+ *   3 A        device, in: the matrices; out: L (unit diagonal not stored)
+ *              below the diagonal and U on and above it, rows in pivoted order
+ *   4 lda      >= max(1, n)
+ *   5 strideA  elements between matrices, >= lda*n when batch > 1
+ *   6 ipiv     device int32, out: strideP entries per matrix, first n written
+ *   7 strideP  >= n when batch > 1
+ *   8 info     device int32[batch], out
+ *   9 batch    >= 0
+ *  10 stream
+ * Follows: BatchLAS "LU" page, getrf rows of the family table and the tiny,
+ * cta and blocked paragraphs.
+ */
+int batchlu_getrf(batchlu_dtype t, int n, void* A, int lda, long long strideA,
+                  int* ipiv, long long strideP, int* info, int batch,
+                  hipStream_t stream);
+
+/*
+ * batchlu_getrs -- solve op(A) X = B with the factors and ipiv of batchlu_getrf.
+ *   1 t, 2 trans ('N' only; 'T'/'C' return BATCHLU_ERR_UNSUPPORTED),
+ *   3 n, 4 nrhs >= 0, 5 A (device, read only), 6 lda, 7 strideA,
+ *   8 ipiv (device, read only), 9 strideP,
+ *  10 B (device, in: right-hand sides, out: X), 11 ldb >= max(1, n),
+ *  12 strideB >= ldb*nrhs when batch > 1, 13 batch, 14 stream.
+ * The factors of a matrix whose info was > 0 give inf/NaN, as in LAPACK.
+ * Follows: BatchLAS "LU" page, getrs paragraphs (permutation, then forward
+ * substitution with unit-lower L, then back substitution with U).
+ */
+int batchlu_getrs(batchlu_dtype t, char trans, int n, int nrhs, const void* A,
+                  int lda, long long strideA, const int* ipiv,
+                  long long strideP, void* B, int ldb, long long strideB,
+                  int batch, hipStream_t stream);
+
+/*
+ * batchlu_gesv -- factor and solve: getrf on A, then getrs on B.
+ *   1 t, 2 n, 3 nrhs, 4 A, 5 lda, 6 strideA, 7 ipiv, 8 strideP,
+ *   9 B, 10 ldb, 11 strideB, 12 info, 13 batch, 14 stream.
+ * A matrix with info[b] > 0 keeps its B unchanged (LAPACK gesv behaviour).
+ * Follows: BatchLAS "LU" page, gesv rows of the family table (a fused
+ * factor-and-solve for small n; getrf then getrs otherwise).
+ */
+int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda,
+                 long long strideA, int* ipiv, long long strideP, void* B,
+                 int ldb, long long strideB, int* info, int batch,
+                 hipStream_t stream);
+
+/*
+ * batchlu_select_tier -- the tier an AUTO call would use for this shape
+ * (op: 0 getrf, 1 getrs, 2 gesv), or BATCHLU_ERR_CAPACITY / -k on bad
+ * arguments.  Host only, launches nothing.  Follows: BatchLAS "LU" page,
+ * routing tables (a rank of tiers per shape).
+ */
+int batchlu_select_tier(batchlu_dtype t, int op, int n, int nrhs, int batch);
+
+/*
+ * batchlu_set_tier -- pin every later call in this process to one tier
+ * (BATCHLU_TIER_*; AUTO restores the selector).  For tests and A/B timing.
+ * A pinned tier that cannot run a shape makes the call return
+ * BATCHLU_ERR_CAPACITY.  Returns the previous setting.
+ */
+int batchlu_set_tier(int tier);
+
+/* Human-readable name of a status code. */
+const char* batchlu_status_string(int status);
+
+/* Library version string. */
+const char* batchlu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BATCHLU_H */

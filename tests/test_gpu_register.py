@@ -1,0 +1,197 @@
+"""GPU parity of the register tiers (tiny: n <= 32, cta: 32 < n <= 64) and of
+the direct getrs kernel against the CPU oracle, through the C ABI.
+
+Bar: ipiv and info identical, L and U bit-identical (these tiers perform the
+oracle's exact operation sequence), X within the solve-residual bound
+||A x - b|| / (n eps ||A|| ||x||) <= 20 and close to the oracle's X (the back
+substitution multiplies by one reciprocal per diagonal entry where the oracle
+divides, so X may differ in the last bits)."""
+import numpy as np
+import pytest
+
+import lu_inputs
+import oracle
+from gpu_support import bits, gesv_gpu, gpu_available, matrices_equal_bits, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    import dense_linear_algebra_amd as lib
+else:   # collected without a GPU only when someone runs -m gpu by mistake
+    lib = None
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    lib.batchlu_set_tier(lib.TIER_AUTO)
+    yield
+    lib.batchlu_set_tier(lib.TIER_AUTO)
+
+
+def _check_solution(A, B, X, n, nrhs, batch, info, Xo, sample=None, lda=None, sA=None, ldb=None, sB=None):
+    lda = n if lda is None else lda
+    sA = lda * n if sA is None else sA
+    ldb = n if ldb is None else ldb
+    sB = ldb * nrhs if sB is None else sB
+    eps = oracle.eps_of(A.dtype)
+    idx = range(batch) if sample is None else sample
+    worst = 0.0
+    for b in idx:
+        if info[b] != 0:
+            continue
+        Am = oracle.matrix(A, b, n, n, lda, sA)
+        Bm = oracle.matrix(B, b, n, nrhs, ldb, sB)
+        Xm = oracle.matrix(X, b, n, nrhs, ldb, sB)
+        Xom = oracle.matrix(Xo, b, n, nrhs, ldb, sB)
+        res = oracle.solve_residual(Am, Xm, Bm)
+        assert res <= 20, f"matrix {b}: solve residual {res}"
+        # forward-error agreement with the oracle, scaled by the conditioning
+        cond = np.linalg.cond(Am.astype(np.complex128))
+        err = np.max(np.abs(Xm - Xom)) / max(np.max(np.abs(Xom)), 1e-300)
+        worst = max(worst, err / (n * eps * cond))
+        assert err <= 8 * n * eps * cond, f"matrix {b}: |X - X_oracle| = {err}, cond {cond}"
+    return worst
+
+
+CASES = (
+    [(np.float32, n, r) for n in (1, 2, 3, 4, 5, 8, 9, 13, 16, 17, 24, 31, 32, 33, 48, 64) for r in (1, 3, 8)]
+    + [(np.float32, n, 16) for n in (7, 16, 32, 64)]
+    + [(np.float64, n, r) for n in (2, 6, 16, 17, 32, 40, 64) for r in (1, 8)]
+    + [(np.complex64, n, r) for n in (3, 8, 16, 21, 32, 64) for r in (1, 16)]
+    + [(np.complex128, n, r) for n in (4, 11, 16, 32) for r in (1, 8)]
+)
+
+
+@pytest.mark.parametrize("dtype,n,nrhs", CASES, ids=lambda v: getattr(v, "__name__", str(v)))
+def test_register_gesv_matches_oracle(dtype, n, nrhs):
+    batch = 131   # not a multiple of any matrices-per-block count: ragged last block
+    A, B = lu_inputs.random_problem(1000 + 7 * n + nrhs, dtype, n, nrhs, batch)
+    print(f"case gesv dtype={np.dtype(dtype).name} n={n} nrhs={nrhs} batch={batch}", flush=True)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch)
+    oA, oB, oP, oI, _ = oracle_run(A, B, n, nrhs, batch)
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+    _check_solution(A, B, gB, n, nrhs, batch, oI, oB)
+
+
+@pytest.mark.parametrize("dtype,n", [(np.float32, 5), (np.float32, 32), (np.float32, 64), (np.float64, 32),
+                                     (np.complex64, 64), (np.complex128, 32)])
+def test_register_getrf_matches_oracle(dtype, n):
+    batch = 70
+    A, _ = lu_inputs.random_problem(2000 + n, dtype, n, 0, batch)
+    gA, _, gP, gI = gesv_gpu(lib, A, None, n, 0, batch, op="getrf")
+    oA, _, oP, oI, _ = oracle_run(A, None, n, 0, batch, op="getrf")
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+
+
+@pytest.mark.parametrize("dtype,n,nrhs", [(np.float32, 16, 1), (np.float32, 32, 8), (np.float32, 45, 3),
+                                          (np.float64, 20, 8), (np.complex64, 64, 16), (np.complex128, 9, 1)])
+def test_register_padded_layout_keeps_poison(dtype, n, nrhs):
+    """lda = n + 3, ldb = n + 2, batch strides larger than ld*cols, strideP > n:
+    results match the dense run and the pads keep their poison."""
+    batch = 19
+    lda, ldb, sP = n + 3, n + 2, n + 5
+    sA, sB = lda * n + 7, ldb * nrhs + 5
+    A, B = lu_inputs.random_problem(3000 + n, dtype, n, nrhs, batch)
+    poison = 1.0e30
+    Ap = lu_inputs.relayout(A, n, n, batch, n, n * n, lda, sA, poison)
+    Bp = lu_inputs.relayout(B, n, nrhs, batch, n, n * nrhs, ldb, sB, poison)
+    gA, gB, gP, gI = gesv_gpu(lib, Ap, Bp, n, nrhs, batch, lda=lda, sA=sA, ldb=ldb, sB=sB, sP=sP)
+    oA, oB, oP, oI, _ = oracle_run(A, B, n, nrhs, batch)
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert np.all(gP[:, n:] == -7), "ipiv written past n"
+    back = lu_inputs.relayout(gA, n, n, batch, lda, sA, n, n * n)
+    assert matrices_equal_bits(back, oA, n, n, n, n * n, batch) == []
+    for buf, ld, st, cols in ((gA, lda, sA, n), (gB, ldb, sB, nrhs)):
+        mask = np.ones(buf.size, bool)
+        for b in range(batch):
+            for j in range(cols):
+                mask[b * st + j * ld: b * st + j * ld + n] = False
+        assert np.all(buf[mask] == poison), "a pad element was written"
+    Xd = lu_inputs.relayout(gB, n, nrhs, batch, ldb, sB, n, n * nrhs)
+    _check_solution(A, B, Xd, n, nrhs, batch, oI, oB)
+
+
+def _one(M, dtype):
+    return np.ascontiguousarray(np.asarray(M, dtype=dtype).T).reshape(-1).copy()
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64, np.complex64])
+@pytest.mark.parametrize("n", [8, 32, 64])
+def test_register_special_matrices(dtype, n):
+    """Wilkinson growth (all ties), a zero column (info), a singular last
+    step, a NaN column and an Inf entry, mixed in one batch with a random
+    matrix: per-matrix ipiv/info/LU parity, and B untouched where info > 0."""
+    rng = np.random.default_rng(n)
+    mats = []
+    W = np.tril(-np.ones((n, n)), -1) + np.eye(n)
+    W[:, -1] = 1
+    mats.append(W)
+    Z = rng.uniform(-1, 1, (n, n))
+    Z[:, min(3, n - 1)] = 0
+    mats.append(Z)
+    S = rng.uniform(-1, 1, (n, n))
+    S[-1, :] = 0
+    mats.append(S)
+    N = rng.uniform(-1, 1, (n, n))
+    N[min(2, n - 1), 0] = np.nan
+    mats.append(N)
+    I = rng.uniform(-1, 1, (n, n))
+    I[n // 2, n // 3] = -np.inf
+    mats.append(I)
+    mats.append(rng.uniform(-1, 1, (n, n)))
+    batch, nrhs = len(mats), 2
+    A = np.concatenate([_one(M, dtype) for M in mats])
+    B = rng.uniform(-1, 1, batch * n * nrhs).astype(dtype)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch)
+    oA, oB, oP, oI, _ = oracle_run(A, B, n, nrhs, batch)
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+    assert oI[1] > 0 and oI[2] == n
+    for b in range(batch):
+        if oI[b] > 0:
+            np.testing.assert_array_equal(bits(gB[b * n * nrhs:(b + 1) * n * nrhs]),
+                                          bits(B[b * n * nrhs:(b + 1) * n * nrhs]))
+
+
+@pytest.mark.parametrize("dtype,n,nrhs", [(np.float32, 7, 5), (np.float32, 32, 8), (np.float32, 64, 33),
+                                          (np.float64, 50, 3), (np.complex64, 64, 16), (np.complex128, 30, 2)])
+def test_getrs_direct_matches_oracle_bitwise(dtype, n, nrhs):
+    """batchlu_getrs on the GPU factors: the direct solve performs the
+    oracle's operation order (division by u_kk), so X is bit-identical to
+    the oracle's getrs applied to the same factors."""
+    batch = 23
+    A, B = lu_inputs.random_problem(4000 + n, dtype, n, nrhs, batch)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch, op="getrf+getrs")
+    oB = B.copy()
+    oracle.getrs(gA, n, n, n * n, gP[:, :n], oB, nrhs, n, n * nrhs, batch)
+    assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
+
+
+@pytest.mark.parametrize("name", ["sgesv_n16_b1024", "sgesv_n32_r8_b32768", "cgesv_n64_r16_b8192"])
+def test_full_size_workloads(name):
+    """The register-tier workloads at their full batch, in the launch
+    configuration the benchmark times: every matrix checked."""
+    w = lu_inputs.WORKLOADS[name]
+    A, B = lu_inputs.dense_problem(w)
+    print(f"case full {name}", flush=True)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, w.n, w.nrhs, w.batch)
+    oA, oB, oP, oI, _ = oracle_run(A, B, w.n, w.nrhs, w.batch)
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :w.n], oP)
+    assert matrices_equal_bits(gA, oA, w.n, w.n, w.n, w.n * w.n, w.batch) == []
+    rng = np.random.default_rng(0)
+    sample = sorted(set(rng.integers(0, w.batch, 64).tolist()) | {0, w.batch - 1})
+    _check_solution(A, B, gB, w.n, w.nrhs, w.batch, oI, oB, sample=sample)
+
+
+def test_selected_tiers():
+    assert lib.batchlu_select_tier(lib.R32, 2, 32, 8, 32768) == lib.TIER_TINY
+    assert lib.batchlu_select_tier(lib.C64, 2, 64, 16, 8192) == lib.TIER_CTA
