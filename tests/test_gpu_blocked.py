@@ -1,0 +1,154 @@
+"""GPU parity of the blocked tier (panel 32, fused right interchange + TRSM,
+MFMA trailing update for real types, deferred left interchange) and of the
+blocked getrs, against the CPU oracle through the C ABI.
+
+Bar: ipiv and info identical and L, U bit-identical (the blocked update
+chains one fused multiply-add per k in ascending order, as the unblocked
+oracle does; an MFMA 16x16x4 accumulates exactly that way, which the
+f32/f64 cases here check at scale); getrs X bit-identical to the oracle's
+getrs on the same factors (same order, true division by u_kk)."""
+import numpy as np
+import pytest
+
+import lu_inputs
+import oracle
+from gpu_support import bits, gesv_gpu, gpu_available, matrices_equal_bits, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    import dense_linear_algebra_amd as lib
+else:
+    lib = None
+
+
+@pytest.fixture(autouse=True)
+def _blocked_tier():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    lib.batchlu_set_tier(lib.TIER_BLOCKED)
+    yield
+    lib.batchlu_set_tier(lib.TIER_AUTO)
+
+
+CASES = ([(np.float32, n) for n in (1, 7, 32, 33, 64, 65, 100, 161, 256)]
+         + [(np.float64, n) for n in (31, 64, 96, 130, 256)]
+         + [(np.complex64, n) for n in (40, 64, 100)]
+         + [(np.complex128, n) for n in (33, 70)])
+
+
+@pytest.mark.parametrize("dtype,n", CASES, ids=lambda v: getattr(v, "__name__", str(v)))
+def test_blocked_getrf_matches_oracle(dtype, n):
+    batch = 5
+    A, _ = lu_inputs.random_problem(6000 + n, dtype, n, 0, batch)
+    print(f"case blocked getrf dtype={np.dtype(dtype).name} n={n}", flush=True)
+    gA, _, gP, gI = gesv_gpu(lib, A, None, n, 0, batch, op="getrf")
+    oA, _, oP, oI, _ = oracle_run(A, None, n, 0, batch, op="getrf")
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+
+
+@pytest.mark.parametrize("dtype,n,nrhs", [(np.float32, 100, 3), (np.float32, 256, 33), (np.float64, 130, 5),
+                                          (np.complex64, 70, 2), (np.complex128, 40, 3)])
+def test_blocked_getrs_matches_oracle_bitwise(dtype, n, nrhs):
+    batch = 4
+    A, B = lu_inputs.random_problem(7000 + n, dtype, n, nrhs, batch)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch, op="getrf+getrs")
+    oB = B.copy()
+    oracle.getrs(gA, n, n, n * n, gP[:, :n], oB, nrhs, n, n * nrhs, batch)
+    assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
+    for b in range(batch):
+        Am = oracle.matrix(A, b, n, n, n, n * n)
+        assert oracle.solve_residual(Am, oracle.matrix(gB, b, n, nrhs, n, n * nrhs),
+                                     oracle.matrix(B, b, n, nrhs, n, n * nrhs)) <= 20
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_blocked_gesv_matches_oracle(dtype):
+    n, nrhs, batch = 97, 4, 6
+    A, B = lu_inputs.random_problem(7100, dtype, n, nrhs, batch)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch)
+    oA, oB, oP, oI, _ = oracle_run(A, B, n, nrhs, batch)
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+    assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
+
+
+def _one(M, dtype):
+    return np.ascontiguousarray(np.asarray(M, dtype=dtype).T).reshape(-1).copy()
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64, np.complex64])
+def test_blocked_special_matrices(dtype):
+    """Wilkinson growth across three panels (every step a tie), a zero column
+    inside the second panel (info from a later panel), a singular last step
+    and a NaN; B untouched where info > 0."""
+    n, nrhs = 90, 2
+    rng = np.random.default_rng(3)
+    W = np.tril(-np.ones((n, n)), -1) + np.eye(n)
+    W[:, -1] = 1
+    Z = rng.uniform(-1, 1, (n, n))
+    Z[:, 45] = 0
+    S = rng.uniform(-1, 1, (n, n))
+    S[-1, :] = 0
+    N = rng.uniform(-1, 1, (n, n))
+    N[70, 50] = np.nan
+    mats = [W, Z, S, N, rng.uniform(-1, 1, (n, n))]
+    batch = len(mats)
+    A = np.concatenate([_one(M, dtype) for M in mats])
+    B = rng.uniform(-1, 1, batch * n * nrhs).astype(dtype)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch)
+    oA, oB, oP, oI, _ = oracle_run(A, B, n, nrhs, batch)
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+    assert oI[1] == 46 and oI[2] == n
+    for b in range(batch):
+        if oI[b] > 0:
+            np.testing.assert_array_equal(bits(gB[b * n * nrhs:(b + 1) * n * nrhs]),
+                                          bits(B[b * n * nrhs:(b + 1) * n * nrhs]))
+
+
+@pytest.mark.parametrize("dtype,n,nrhs", [(np.float32, 75, 3), (np.float64, 66, 1), (np.complex64, 41, 2)])
+def test_blocked_padded_layout_keeps_poison(dtype, n, nrhs):
+    batch = 3
+    lda, ldb, sP = n + 5, n + 1, n + 3
+    sA, sB = lda * n + 11, ldb * nrhs + 3
+    A, B = lu_inputs.random_problem(7200 + n, dtype, n, nrhs, batch)
+    poison = 1.0e30
+    Ap = lu_inputs.relayout(A, n, n, batch, n, n * n, lda, sA, poison)
+    Bp = lu_inputs.relayout(B, n, nrhs, batch, n, n * nrhs, ldb, sB, poison)
+    gA, gB, gP, gI = gesv_gpu(lib, Ap, Bp, n, nrhs, batch, lda=lda, sA=sA, ldb=ldb, sB=sB, sP=sP)
+    oA, oB, oP, oI, _ = oracle_run(A, B, n, nrhs, batch)
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert np.all(gP[:, n:] == -7)
+    back = lu_inputs.relayout(gA, n, n, batch, lda, sA, n, n * n)
+    assert matrices_equal_bits(back, oA, n, n, n, n * n, batch) == []
+    Xd = lu_inputs.relayout(gB, n, nrhs, batch, ldb, sB, n, n * nrhs)
+    assert matrices_equal_bits(Xd, oB, n, nrhs, n, n * nrhs, batch) == []
+    for buf, ld, st, cols in ((gA, lda, sA, n), (gB, ldb, sB, nrhs)):
+        mask = np.ones(buf.size, bool)
+        for b in range(batch):
+            for j in range(cols):
+                mask[b * st + j * ld: b * st + j * ld + n] = False
+        assert np.all(buf[mask] == poison)
+
+
+@pytest.mark.parametrize("name", ["dgesv_n256_b1024", "sgetrf_sgetrs_n1024_r32_b64"])
+def test_blocked_full_size_workloads(name):
+    """The blocked-tier workloads at their full batch under automatic tier
+    selection, every matrix compared: ipiv, info and LU bit-identical, X
+    bit-identical to the oracle's solve."""
+    lib.batchlu_set_tier(lib.TIER_AUTO)
+    w = lu_inputs.WORKLOADS[name]
+    A, B = lu_inputs.dense_problem(w)
+    print(f"case full {name}", flush=True)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, w.n, w.nrhs, w.batch, op="gesv" if w.op == "gesv" else "getrf+getrs")
+    oA, oB, oP, oI, _ = oracle_run(A, B, w.n, w.nrhs, w.batch, op="gesv" if w.op == "gesv" else "getrf+getrs")
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :w.n], oP)
+    assert matrices_equal_bits(gA, oA, w.n, w.n, w.n, w.n * w.n, w.batch) == []
+    assert matrices_equal_bits(gB, oB, w.n, w.nrhs, w.n, w.n * w.nrhs, w.batch) == []
