@@ -30,7 +30,8 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 FP64_PEAK_TFLOPS = 78.6
 METRIC = "batched gesv matrices/s + GFLOP/s (n=32 f32, n=256 f64), % of roofline"
 KERNEL_SOURCES = {
-    "register": ["dense_linear_algebra_amd/csrc/register_lu_kernel.h", "dense_linear_algebra_amd/csrc/device_ops.h"],
+    "register": ["dense_linear_algebra_amd/csrc/register_lu_kernel.h", "dense_linear_algebra_amd/csrc/register_lu_row16.h",
+                 "dense_linear_algebra_amd/csrc/device_ops.h"],
 }
 
 
@@ -70,6 +71,57 @@ def traffic_from_profile(workload: str, kind: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(db: str):
+    """(kernel name, dispatch id, counter value) rows of one rocprofv3 --pmc
+    database, read through rocpd2csv."""
+    import csv
+    import subprocess
+    import tempfile
+    out = os.path.join(tempfile.mkdtemp(), "csv")
+    subprocess.run(["/opt/rocm/bin/rocpd2csv", "-i", os.path.abspath(db), "-d", out], check=True,
+                   capture_output=True, cwd="/tmp")
+    rows = {}
+    with open(os.path.join(out, "out_counter_collection_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            key = int(r["Dispatch_Id"])
+            name, val = r["Kernel_Name"], float(r["Counter_Value"])
+            rows[key] = (name, rows.get(key, (name, 0.0))[1] + val)
+    return rows
+
+
+def write_counter_summary(workload: str, kind: str, kernel: str, fetch_db: str, write_db: str,
+                          copy_mb: int, commands):
+    """HBM bytes per launch of `kernel` from a FETCH_SIZE and a WRITE_SIZE run,
+    each scaled by what the counter reads for the plain device copy of
+    copy_mb MiB that the same run made first (bench.py --copy-probe-mb)."""
+    w = lu_inputs.WORKLOADS[workload]
+    res = {"kernel": kernel, "workload": workload, "source_hash": source_hash(kind), "commands": list(commands)}
+    per = {}
+    for tag, db in (("fetch", fetch_db), ("write", write_db)):
+        rows = _counter_rows(db)
+        copies = [v for n, v in rows.values() if n.startswith("__amd_rocclr_copyBuffer")]
+        mine = [v for n, v in rows.values() if kernel in n]
+        if not copies or not mine:
+            raise SystemExit(f"{db}: no copy probe or no '{kernel}' dispatch")
+        per[tag] = (sum(mine) / len(mine), max(copies))
+    nbytes = copy_mb << 20
+    fetch_scale = nbytes / (per["fetch"][1] * 1024.0)
+    write_scale = nbytes / (per["write"][1] * 1024.0)
+    rd = per["fetch"][0] * 1024.0 * fetch_scale
+    wr = per["write"][0] * 1024.0 * write_scale
+    alg = algorithmic_bytes(w) * w.batch
+    res.update({
+        "fetch_size_kib_per_dispatch": per["fetch"][0], "write_size_kib_per_dispatch": per["write"][0],
+        "copy_probe": {"bytes_read": nbytes, "bytes_written": nbytes, "fetch_size_kib": per["fetch"][1],
+                       "write_size_kib": per["write"][1], "fetch_scale": fetch_scale, "write_scale": write_scale},
+        "hbm_bytes_read_per_launch": rd, "hbm_bytes_written_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
+        "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": (rd + wr) / alg})
+    path = os.path.join(ROOT, "profiles", f"{kind}_gesv_{workload}_counters.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    print(path)
+
+
 def cpu_baseline(w, A, B, budget_s: float = 10.0):
     """The oracle (as is) on host cores: whole-batch gesv repeated until about
     budget_s of wall time has elapsed."""
@@ -96,7 +148,18 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this size first (reference for HBM counters)")
+    ap.add_argument("--counters-summary", nargs=3, metavar=("KERNEL", "FETCH_DB", "WRITE_DB"),
+                    help="write the HBM-traffic summary of KERNEL from two rocprofv3 --pmc databases "
+                         "(FETCH_SIZE, WRITE_SIZE) taken with --copy-probe-mb; no GPU needed")
     args = ap.parse_args()
+    if args.counters_summary:
+        kern, fdb, wdb = args.counters_summary
+        mb = args.copy_probe_mb or 256
+        base = f"python3 bench.py --workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mb {mb}"
+        write_counter_summary(args.workload, "register", kern, fdb, wdb, mb,
+                              [f"rocprofv3 --pmc FETCH_SIZE -d <dir> -o f -- {base}",
+                               f"rocprofv3 --pmc WRITE_SIZE -d <dir> -o w -- {base}"])
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: every matrix is independent, so more GPUs would each "

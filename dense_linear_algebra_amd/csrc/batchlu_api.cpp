@@ -46,14 +46,14 @@ bool tier_can_run(int tier, int t, int op, int n, int nrhs) {
     case BATCHLU_TIER_TINY:
     case BATCHLU_TIER_CTA: {
         const bool one_wave = tier == BATCHLU_TIER_CTA;
-        if (op == OP_GETRS) return getrs_direct_supported(t, n, nrhs) && n <= 64;
+        if (op == OP_GETRS) return getrs_rows_supported(t, n) && n <= 64;
         if (op == OP_GESV) return register_supported(t, n, nrhs, MODE_GESV, one_wave) ||
                                   (register_supported(t, n, 0, MODE_GETRF, one_wave) &&
-                                   getrs_direct_supported(t, n, nrhs));
+                                   getrs_rows_supported(t, n));
         return register_supported(t, n, 0, MODE_GETRF, one_wave);
     }
     case BATCHLU_TIER_BLOCKED:
-        if (op == OP_GETRS) return blocked_supported(t, n) || getrs_direct_supported(t, n, nrhs);
+        if (op == OP_GETRS) return blocked_supported(t, n) || getrs_rows_supported(t, n);
         return blocked_supported(t, n);
     default:
         return false;
@@ -84,9 +84,12 @@ int run_getrf(int tier, int t, const Problem& p, hipStream_t s) {
     }
 }
 
+// The one-launch solve covers n <= 1024; larger orders use the blocked
+// sequence of triangular-block solves and GEMM updates.
 int run_getrs(int tier, int t, const Problem& p, hipStream_t s) {
-    if (tier == BATCHLU_TIER_BLOCKED && blocked_supported(t, p.n)) return status_of(blocked_getrs(t, p, s));
-    return status_of(getrs_direct_launch(t, p, s));
+    (void)tier;
+    if (getrs_rows_supported(t, p.n)) return status_of(getrs_rows_launch(t, p, s));
+    return status_of(blocked_getrs(t, p, s));
 }
 
 }  // namespace

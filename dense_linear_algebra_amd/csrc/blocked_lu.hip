@@ -486,7 +486,10 @@ __global__ void __launch_bounds__(1024) permute_rows_kernel(Problem p)
     const int tid = threadIdx.x, nt = blockDim.x;
     const long long mat = blockIdx.x;
     if (p.info && p.info[mat] != 0) return;
-    for (int i = tid; i < n; i += nt) sipiv[i] = p.ipiv[mat * p.sP + i] - 1;
+    for (int i = tid; i < n; i += nt) {   // entries outside 1..n: no interchange
+        const int v = p.ipiv[mat * p.sP + i] - 1;
+        sipiv[i] = (v >= 0 && v < n) ? v : i;
+    }
     __syncthreads();
     for (int i = tid; i < n; i += nt) {
         int x = i;

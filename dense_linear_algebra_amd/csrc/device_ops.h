@@ -143,6 +143,23 @@ __device__ inline uint64_t pivot_key(double m) {
 }
 
 // ---------------------------------------------------------------------------
+// v_readlane for every element type (the lane index must be wavefront-uniform)
+// ---------------------------------------------------------------------------
+__device__ inline float readlane_t(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ inline double readlane_t(double v, int l) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <typename R>
+__device__ inline cplx<R> readlane_t(cplx<R> v, int l) {
+    return cplx<R>{readlane_t(v.re, l), readlane_t(v.im, l)};
+}
+
+// ---------------------------------------------------------------------------
 // all-reduce over aligned groups of G lanes inside a wave64.  Stage order
 // matters: quad_perm swaps (xor 1, xor 2), then row_half_mirror and
 // row_mirror (valid once each quad / half row already agrees), then

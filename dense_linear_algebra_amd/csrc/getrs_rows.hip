@@ -1,0 +1,207 @@
+// getrs_rows.hip -- the whole LU solve of one matrix and one tile of
+// right-hand sides in a single work-group: one row per thread, n <= 1024.
+//
+// BatchLAS "LU" page, fused getrs paragraph (one work-group per matrix does
+// the permutation and both substitutions in one launch) and blocked getrs
+// (block solves then updates); here the two are combined for gfx950:
+//   - the interchange list is applied as one gather (a backward trace of
+//     ipiv per row), so no row is written before every row has been read;
+//   - forward: per block of 32 rows, the wavefront holding those rows solves
+//     the 32 x 32 unit-lower block on its own (x_m broadcast by readlane, no
+//     barrier), publishes the block's solution in LDS, and after one barrier
+//     every lower row subtracts l_ik * y_k for the block's 32 k;
+//   - back: the same with U, blocks descending, true division by u_kk.
+// Per element the order of operations is the plain one (ascending k forward,
+// descending k backward), so X equals the unblocked substitution bit for bit.
+#include "device_ops.h"
+#include "internal.h"
+
+namespace batchlu {
+
+namespace {
+
+constexpr int BS = 32;   // rows per diagonal block
+constexpr int CK = 8;    // columns of L or U loaded per round
+
+template <typename T, int NRT>
+__global__ void __launch_bounds__(1024) getrs_rows_kernel(Problem p, int rtiles)
+{
+    using O = ops<T>;
+    extern __shared__ uint4 smem_raw[];
+    int* sipiv = (int*)smem_raw;                                             // n entries
+    T* ybuf = (T*)((char*)smem_raw + ((p.n * 4 + 15) / 16) * 16);            // [2][BS][NRT]
+
+    const int n = p.n;
+    const long long m = blockIdx.x / rtiles;
+    const int c0 = (int)(blockIdx.x % rtiles) * NRT;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    if (p.info && p.info[m] != 0) return;   // composed gesv: failed factorisation keeps B
+
+    const T* LU = (const T*)p.A + m * p.sA;
+    const int* ipiv = p.ipiv + m * p.sP;
+    T* B = (T*)p.B + m * p.sB;
+
+    for (int i = tid; i < n; i += blockDim.x) {   // entries outside 1..n: no interchange
+        const int v = ipiv[i] - 1;
+        sipiv[i] = (v >= 0 && v < n) ? v : i;
+    }
+    __syncthreads();
+
+    // a8: row tid of P*B is original row src
+    const int row = tid;
+    const bool have = row < n;
+    T y[NRT];
+    {
+        int src = row;
+        if (have)
+            for (int k = n - 1; k >= 0; --k) {
+                const int pk = sipiv[k];
+                src = (src == k) ? pk : (src == pk ? k : src);
+            }
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
+            y[r] = (have && c0 + r < p.nrhs) ? B[src + (long long)(c0 + r) * p.ldb] : O::zero();
+    }
+
+    const int P = (n + BS - 1) / BS;
+    // a9: forward, L unit lower
+    for (int kb = 0; kb < P; ++kb) {
+        const int r0 = kb * BS;
+        const int w = min(BS, n - r0);
+        T* yb = ybuf + (size_t)(kb & 1) * BS * NRT;
+        if (wave == r0 / 64) {
+            // the 32 rows of the block are lanes r0%64 .. r0%64+w-1 of this wavefront
+            const int base = r0 % 64;
+            const int mrow = lane - base;      // row inside the block when in [0, w)
+#pragma unroll
+            for (int cc = 0; cc < BS; cc += CK) {
+                T lrow[CK];
+#pragma unroll
+                for (int e = 0; e < CK; ++e) {
+                    const int c = cc + e;
+                    lrow[e] = (mrow > c && mrow < w) ? LU[row + (long long)(r0 + c) * p.lda] : O::zero();
+                }
+#pragma unroll
+                for (int e = 0; e < CK; ++e) {
+                    const int c = cc + e;
+                    if (c >= w) continue;
+                    T xc[NRT];
+#pragma unroll
+                    for (int r = 0; r < NRT; ++r) xc[r] = readlane_t(y[r], base + c);
+                    if (mrow > c && mrow < w)
+#pragma unroll
+                        for (int r = 0; r < NRT; ++r) O::fms(y[r], lrow[e], xc[r]);
+                }
+            }
+            if (mrow >= 0 && mrow < w)
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) yb[mrow * NRT + r] = y[r];
+        }
+        __syncthreads();
+        if (have && row >= r0 + w) {
+#pragma unroll
+            for (int cc = 0; cc < BS; cc += CK) {
+                T lrow[CK];
+#pragma unroll
+                for (int e = 0; e < CK; ++e)
+                    lrow[e] = cc + e < w ? LU[row + (long long)(r0 + cc + e) * p.lda] : O::zero();
+#pragma unroll
+                for (int e = 0; e < CK; ++e) {
+                    if (cc + e >= w) continue;
+#pragma unroll
+                    for (int r = 0; r < NRT; ++r) O::fms(y[r], lrow[e], yb[(cc + e) * NRT + r]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // a10: back, U upper; blocks descending
+    for (int kb = P - 1; kb >= 0; --kb) {
+        const int r0 = kb * BS;
+        const int w = min(BS, n - r0);
+        T* yb = ybuf + (size_t)(kb & 1) * BS * NRT;
+        if (wave == r0 / 64) {
+            const int base = r0 % 64;
+            const int mrow = lane - base;
+#pragma unroll
+            for (int cc = BS - CK; cc >= 0; cc -= CK) {
+                T urow[CK];
+#pragma unroll
+                for (int e = 0; e < CK; ++e) {
+                    const int c = cc + e;
+                    urow[e] = (mrow >= 0 && mrow <= c && c < w) ? LU[row + (long long)(r0 + c) * p.lda] : O::zero();
+                }
+#pragma unroll
+                for (int e = CK - 1; e >= 0; --e) {
+                    const int c = cc + e;
+                    if (c >= w) continue;
+                    if (mrow == c)
+#pragma unroll
+                        for (int r = 0; r < NRT; ++r) y[r] = O::div(y[r], urow[e]);
+                    T xc[NRT];
+#pragma unroll
+                    for (int r = 0; r < NRT; ++r) xc[r] = readlane_t(y[r], base + c);
+                    if (mrow >= 0 && mrow < c)
+#pragma unroll
+                        for (int r = 0; r < NRT; ++r) O::fms(y[r], urow[e], xc[r]);
+                }
+            }
+            if (mrow >= 0 && mrow < w)
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) yb[mrow * NRT + r] = y[r];
+        }
+        __syncthreads();
+        if (have && row < r0) {
+#pragma unroll
+            for (int cc = BS - CK; cc >= 0; cc -= CK) {
+                T urow[CK];
+#pragma unroll
+                for (int e = 0; e < CK; ++e)
+                    urow[e] = cc + e < w ? LU[row + (long long)(r0 + cc + e) * p.lda] : O::zero();
+#pragma unroll
+                for (int e = CK - 1; e >= 0; --e) {
+                    if (cc + e >= w) continue;
+#pragma unroll
+                    for (int r = 0; r < NRT; ++r) O::fms(y[r], urow[e], yb[(cc + e) * NRT + r]);
+                }
+            }
+        }
+    }
+    if (have)
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
+            if (c0 + r < p.nrhs) B[row + (long long)(c0 + r) * p.ldb] = y[r];
+}
+
+template <typename T, int NRT>
+hipError_t launch_t(const Problem& p, hipStream_t s) {
+    const int threads = ((p.n + 63) / 64) * 64;
+    const int rt = (p.nrhs + NRT - 1) / NRT;
+    const size_t smem = ((p.n * 4 + 15) / 16) * 16 + 2 * BS * NRT * sizeof(T);
+    hipLaunchKernelGGL((getrs_rows_kernel<T, NRT>), dim3((unsigned)((long long)p.batch * rt)), dim3(threads), smem, s,
+                       p, rt);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool getrs_rows_supported(int dtype, int n) {
+    (void)dtype;
+    return n >= 1 && n <= 1024;
+}
+
+hipError_t getrs_rows_launch(int dtype, const Problem& p, hipStream_t s) {
+    if (!getrs_rows_supported(dtype, p.n)) return hipErrorInvalidValue;
+    const bool one = p.nrhs <= 1;
+    switch (dtype) {
+    case R32: return one ? launch_t<float, 1>(p, s) : launch_t<float, 4>(p, s);
+    case R64: return one ? launch_t<double, 1>(p, s) : launch_t<double, 4>(p, s);
+    case C64: return one ? launch_t<cplx<float>, 1>(p, s) : launch_t<cplx<float>, 2>(p, s);
+    case C128: return launch_t<cplx<double>, 1>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace batchlu

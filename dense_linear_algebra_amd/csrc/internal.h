@@ -27,9 +27,11 @@ bool register_supported(int dtype, int n, int nrhs, int mode, bool one_wave_per_
 hipError_t register_launch(int dtype, const Problem& p, int mode, bool one_wave_per_matrix,
                            hipStream_t s);
 
-// Solve with given factors, any n (one work-group per matrix and RHS tile).
-bool getrs_direct_supported(int dtype, int n, int nrhs);
-hipError_t getrs_direct_launch(int dtype, const Problem& p, hipStream_t s);
+// Solve with given factors in one launch (one work-group per matrix and RHS
+// tile, one row per thread), n <= 1024.  With p.info set, matrices whose
+// info is non-zero are skipped (composed gesv).
+bool getrs_rows_supported(int dtype, int n);
+hipError_t getrs_rows_launch(int dtype, const Problem& p, hipStream_t s);
 
 // Blocked right-looking tier (panel, laswp, trsm, gemm) and blocked getrs.
 bool blocked_supported(int dtype, int n);

@@ -25,8 +25,6 @@
 // right-looking LU, so L, U and ipiv are bit-identical to it.
 #pragma once
 
-#include <stdlib.h>
-
 #include "device_ops.h"
 #include "internal.h"
 
@@ -388,7 +386,7 @@ inline Shape pick_shape(int dtype, int n) {
     int nb = n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : n <= 32 ? 32 : 64;
     int rpl;
     switch (dtype) {
-    case R32: rpl = nb <= 8 ? 4 : nb <= 32 ? 2 : 1; break;
+    case R32: rpl = nb <= 8 ? 4 : 1; break;
     case R64: rpl = nb <= 16 ? 2 : 1; break;
     case C64: rpl = nb <= 16 ? 2 : 1; break;
     default: rpl = 1; break;
@@ -431,13 +429,8 @@ hipError_t launch_type(const Problem& p, int mode, hipStream_t s) {
 #define BATCHLU_CASE(NBV, RPLV)                                                  \
     if (sh.nb == NBV && sh.rpl == RPLV) return launch_nr<T, NBV, RPLV>(p, mode, nr, s);
     if constexpr (sizeof(T) == 4) {
-        if (const char* e = getenv("BATCHLU_TINY_RPL")) {   // A/B timing of the partition
-            const int v = atoi(e);
-            if (sh.nb >= 16 && sh.nb <= 32 && (v == 1 || v == 2 || v == 4)) sh.rpl = v;
-        }
-        BATCHLU_CASE(4, 4) BATCHLU_CASE(8, 4) BATCHLU_CASE(16, 4) BATCHLU_CASE(32, 4)
-        BATCHLU_CASE(16, 2) BATCHLU_CASE(32, 2) BATCHLU_CASE(16, 1) BATCHLU_CASE(32, 1)
-        BATCHLU_CASE(64, 1)
+        // orders 9..32 of float go to the 16-lane-row kernel (register_lu_row16.h)
+        BATCHLU_CASE(4, 4) BATCHLU_CASE(8, 4) BATCHLU_CASE(64, 1)
     } else if constexpr (!big) {
         BATCHLU_CASE(4, 2) BATCHLU_CASE(8, 2) BATCHLU_CASE(16, 2) BATCHLU_CASE(32, 1)
         BATCHLU_CASE(64, 1)

@@ -84,7 +84,9 @@ int batchlu_getrf(batchlu_dtype t, int n, void* A, int lda, long long strideA,
  * batchlu_getrs -- solve op(A) X = B with the factors and ipiv of batchlu_getrf.
  *   1 t, 2 trans ('N' only; 'T'/'C' return BATCHLU_ERR_UNSUPPORTED),
  *   3 n, 4 nrhs >= 0, 5 A (device, read only), 6 lda, 7 strideA,
- *   8 ipiv (device, read only), 9 strideP,
+ *   8 ipiv (device, read only; an entry outside 1..n is read as "no
+ *     interchange" so that a corrupt list cannot address rows outside B),
+ *   9 strideP,
  *  10 B (device, in: right-hand sides, out: X), 11 ldb >= max(1, n),
  *  12 strideB >= ldb*nrhs when batch > 1, 13 batch, 14 stream.
  * The factors of a matrix whose info was > 0 give inf/NaN, as in LAPACK.

@@ -64,6 +64,21 @@ def test_blocked_getrs_matches_oracle_bitwise(dtype, n, nrhs):
                                      oracle.matrix(B, b, n, nrhs, n, n * nrhs)) <= 20
 
 
+def test_blocked_getrs_beyond_one_launch_solve():
+    """n > 1024: getrs runs as the blocked sequence of 32-row triangular
+    solves and GEMM updates (ascending k forward, descending k backward)."""
+    n, nrhs, batch = 1100, 3, 2
+    A, B = lu_inputs.random_problem(7300, np.float32, n, nrhs, batch)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch, op="getrf+getrs")
+    oA, _, oP, oI, _ = oracle_run(A, None, n, 0, batch, op="getrf")
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+    oB = B.copy()
+    oracle.getrs(gA, n, n, n * n, gP[:, :n], oB, nrhs, n, n * nrhs, batch)
+    assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
+
+
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_blocked_gesv_matches_oracle(dtype):
     n, nrhs, batch = 97, 4, 6

@@ -163,8 +163,8 @@ def test_register_special_matrices(dtype, n):
 
 @pytest.mark.parametrize("dtype,n,nrhs", [(np.float32, 7, 5), (np.float32, 32, 8), (np.float32, 64, 33),
                                           (np.float64, 50, 3), (np.complex64, 64, 16), (np.complex128, 30, 2)])
-def test_getrs_direct_matches_oracle_bitwise(dtype, n, nrhs):
-    """batchlu_getrs on the GPU factors: the direct solve performs the
+def test_getrs_matches_oracle_bitwise(dtype, n, nrhs):
+    """batchlu_getrs on the GPU factors: the one-launch solve performs the
     oracle's operation order (division by u_kk), so X is bit-identical to
     the oracle's getrs applied to the same factors."""
     batch = 23
