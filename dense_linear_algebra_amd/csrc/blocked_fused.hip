@@ -1,0 +1,526 @@
+// blocked_fused.hip -- blocked right-looking LU (panel width 32) of a real
+// matrix of order n <= 256 in ONE work-group: panel, right interchange, U12
+// solve, MFMA trailing update and the deferred left interchange run as phases
+// of a single kernel, so a matrix stays in the caches of its compute unit
+// between panels instead of streaming the whole batch through HBM once per
+// launch.
+//
+// BatchLAS "LU" page, blocked-getrf, register-panel and row-interchange
+// paragraphs (the same steps and order as the multi-launch blocked tier):
+//   panel   one row per thread in VGPRs, lazy relabel; per column ONE
+//           work-group barrier: every wavefront finds its argmax (DPP inside
+//           rows of 16, readlane across rows, ballot for the winning lane)
+//           and publishes key, position and candidate row to a
+//           double-buffered LDS slot; every thread then reads the four
+//           slots in one round trip and picks the winner;
+//   right   the panel's transpositions reach the trailing columns as one
+//           gather of the new top rows into an LDS stage plus the displaced
+//           rows' moves;
+//   U12     one thread per trailing column solves in the LDS stage,
+//           ascending m, L11 from LDS; the stage then feeds the update and
+//           is written back down each column;
+//   update  A22 -= L21 U12 on v_mfma_{f32,f64}_16x16x4 chained in ascending
+//           k (each MFMA accumulates like four fused multiply-adds in k
+//           order, whichever operand is which), L21 negated; K = 32 always,
+//           since only the last panel can be narrower and it has no trailing
+//           matrix;
+//   left    after the last panel, each earlier panel's L columns are gathered
+//           through the composition of the later interchanges.
+// A zero pivot skips its scaling and its rank-1 update everywhere (U12 solve
+// and trailing update included); the update then runs on the VALU with that
+// k left out, so signed zeros and infinities behave as in the unblocked order.
+#include <type_traits>
+
+#include "device_ops.h"
+#include "internal.h"
+
+namespace batchlu {
+
+namespace {
+
+constexpr int NB = 32;        // panel width
+constexpr int NT = 256;       // threads per work-group = largest order
+constexpr int NW = NT / 64;   // wavefronts
+// LDS stage for U12: CW trailing columns at a time (the widest trailing
+// matrix at once; a narrower stage lets more f64 work-groups share a compute
+// unit's LDS, but their registers already limit them to two)
+template <typename T> struct Stage {
+    static constexpr int CW = NT - NB;
+    static constexpr int SLD = CW + 8;   // padded against bank conflicts
+};
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+// Matrix accesses go through a buffer resource over the matrix's own extent:
+// 32-bit element offsets (one VGPR per address instead of two), and an
+// access outside the extent reads 0 and writes nothing.
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+};
+__device__ inline Buf make_buf(const void* base, uint32_t bytes) {
+    return Buf{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000)};
+}
+__device__ inline float ld(const Buf& b, float*, uint32_t e) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.r, (int)(e * 4u), 0, 0));
+}
+__device__ inline double ld(const Buf& b, double*, uint32_t e) {
+    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(b.r, (int)(e * 8u), 0, 0));
+}
+__device__ inline void st(const Buf& b, uint32_t e, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), b.r, (int)(e * 4u), 0, 0);
+}
+__device__ inline void st(const Buf& b, uint32_t e, double v) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), b.r, (int)(e * 8u), 0, 0);
+}
+
+// work-group barrier that orders LDS only: global stores still in flight are
+// not waited for (used where the next phase reads nothing those stores write)
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// row inside a 16x16 MFMA output block held by (lane group lk, register r)
+template <typename T>
+__device__ inline int mfma_row(int lk, int r) {
+    return sizeof(T) == 4 ? 4 * lk + r : lk + 4 * r;
+}
+
+// maximum over the wavefront, returned wave-uniform: DPP inside each row of
+// 16 lanes, then the four row results by readlane
+__device__ inline uint32_t wave_max(uint32_t v) {
+    v = group_max<16>(v);
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+    return a > b ? a : b;
+}
+// 64-bit keys: the high words first, then the low words among the lanes
+// that hold the maximal high word
+__device__ inline uint64_t wave_max(uint64_t v) {
+    const uint32_t hi = (uint32_t)(v >> 32);
+    const uint32_t mh = wave_max(hi);
+    const uint32_t ml = wave_max(hi == mh ? (uint32_t)v : 0u);
+    return ((uint64_t)mh << 32) | ml;
+}
+
+// argmax over the wavefront: the maximal key (wave-uniform) and the lane that
+// holds it, the lowest position winning among equal keys; win = -1 when no
+// lane holds a candidate (every key 0)
+__device__ inline void tie_break(bool at_max, int pos, int& win) {
+    const int q = group_min<64>(at_max ? pos : 0x7fffffff);
+    win = __builtin_ctzll(__builtin_amdgcn_ballot_w64(pos == q));
+}
+__device__ inline void wave_argmax(uint32_t key, int pos, uint32_t& kmax, int& win) {
+    kmax = wave_max(key);
+    win = -1;
+    if (kmax == 0) return;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(key == kmax);
+    win = __builtin_ctzll(hit);
+    if (__builtin_popcountll(hit) != 1) tie_break(key == kmax, pos, win);
+}
+// 64-bit keys: the high words decide unless several lanes share the maximal
+// high word; only then are the low words reduced
+__device__ inline void wave_argmax(uint64_t key, int pos, uint64_t& kmax, int& win) {
+    const uint32_t hi = (uint32_t)(key >> 32);
+    const uint32_t mh = wave_max(hi);
+    uint64_t hit = __builtin_amdgcn_ballot_w64(hi == mh);
+    win = -1;
+    if (mh != 0 && __builtin_popcountll(hit) == 1) {
+        win = __builtin_ctzll(hit);
+        kmax = ((uint64_t)mh << 32) | (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, win);
+        return;
+    }
+    const uint32_t ml = wave_max(hi == mh ? (uint32_t)key : 0u);
+    kmax = ((uint64_t)mh << 32) | ml;
+    if (kmax == 0) return;
+    hit = __builtin_amdgcn_ballot_w64(key == kmax);
+    win = __builtin_ctzll(hit);
+    if (__builtin_popcountll(hit) != 1) tie_break(key == kmax, pos, win);
+}
+
+
+// WPE: wavefronts per SIMD the registers are budgeted for (= work-groups per
+// compute unit: f32 4; f64 2, which its LDS stage allows as well)
+template <typename T, int WPE>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
+lu_fused_kernel(Problem p, uint32_t extent_bytes)
+{
+    using O = ops<T>;
+    using R = typename O::R;
+    using K = typename O::K;
+    using V = typename std::conditional<sizeof(T) == 4, f32x4_t, f64x4_t>::type;
+    T* const tag = nullptr;   // selects the element type of ld()
+
+    __shared__ K skey[2][NW];
+    __shared__ int spos[2][NW];
+    __shared__ __attribute__((aligned(16))) T cand[2][NW][NB];
+    __shared__ T l11[NB][NB];                // L11 transposed: l11[m][f] = l_fm
+    __shared__ int sipiv[NT];                 // pivot rows, 0-based, global
+    __shared__ int src_top[NB], src_low[NB], dst_low[NB];
+    __shared__ int nlow;
+    constexpr int CW = Stage<T>::CW, SLD = Stage<T>::SLD;
+    __shared__ T S[NB][SLD];                  // P A12, then U12 (rows of the panel x trailing columns)
+
+    const int n = p.n;
+    const uint32_t lda = (uint32_t)p.lda;
+    const int tid0 = threadIdx.x;
+    const long long mat = blockIdx.x;
+    const Buf M = make_buf((T*)p.A + mat * p.sA, extent_bytes);
+    auto at = [&](int i, int j) -> uint32_t { return (uint32_t)i + (uint32_t)j * lda; };
+
+    int info = 0;
+    for (int j0 = 0; j0 < n; j0 += NB) {
+        // the thread index is re-materialised per panel so that no per-thread
+        // address arithmetic is hoisted out of this loop and held live
+        // across every phase (it would cost more registers than it saves)
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        const int w = min(NB, n - j0);
+        const int m = n - j0;                  // panel height
+        // ---- panel: thread tid holds the row at panel position tid --------
+        T a[NB];
+        int pos = tid < m ? tid : 0x3fffffff;
+#pragma unroll
+        for (int c = 0; c < NB; ++c) a[c] = (tid < m && c < w) ? ld(M, tag, at(j0 + tid, j0 + c)) : O::zero();
+        unsigned zmask = 0;
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj) {
+            if (jj >= w) continue;
+            const int buf = jj & 1;
+            const K key = (pos >= jj && pos < m) ? (K)pivot_key(O::metric(a[jj])) : (K)0;
+            K kmax;
+            int win;
+            wave_argmax(key, pos, kmax, win);
+            if (win < 0) {
+                // no candidate row in this wavefront
+                if (lane == 0) {
+                    skey[buf][wave] = 0;
+                    spos[buf][wave] = 0x7fffffff;
+                }
+            } else if (lane == win) {
+                skey[buf][wave] = kmax;
+                spos[buf][wave] = pos;
+                // the candidate row in 16-byte pieces from the piece holding
+                // column jj on (lower columns are written but never read)
+                typedef T vec_t __attribute__((ext_vector_type(16 / sizeof(T))));
+                constexpr int E = 16 / sizeof(T);
+#pragma unroll
+                for (int c = 0; c < NB; c += E) {
+                    if (c + E <= jj) continue;
+                    vec_t v;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) v[e] = a[c + e];
+                    *(vec_t*)&cand[buf][wave][c] = v;
+                }
+            }
+            lds_barrier();
+            // one LDS round trip: the four keys, positions and pivot values
+            K kv[NW];
+            int pv[NW];
+            T cv[NW];
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                kv[v] = skey[buf][v];
+                pv[v] = spos[buf][v];
+                cv[v] = cand[buf][v][jj];
+            }
+            K best = kv[0];
+            int ppos = pv[0], vb = 0;
+            T piv = cv[0];
+#pragma unroll
+            for (int v = 1; v < NW; ++v) {
+                const bool take = kv[v] > best || (kv[v] == best && pv[v] < ppos);
+                best = take ? kv[v] : best;
+                ppos = take ? pv[v] : ppos;
+                vb = take ? v : vb;
+                piv = take ? cv[v] : piv;
+            }
+            // the pivot row is read now, through one VGPR base address and
+            // immediate offsets, so that its reads overlap the reciprocal
+            typedef __attribute__((address_space(3))) const T lds_t;
+            uint32_t rowaddr = (uint32_t)(uintptr_t)(lds_t*)&cand[buf][vb][0];
+            asm volatile("" : "+v"(rowaddr));
+            lds_t* row = (lds_t*)(uintptr_t)rowaddr;
+            T u[NB];
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+                if (c > jj) u[c] = row[c];
+            if (pos == ppos) sipiv[j0 + jj] = j0 + ppos;   // the pivot row's owner records it
+            pos = (pos == ppos) ? jj : (pos == jj ? ppos : pos);
+            const R pm = O::metric(piv);
+            const bool zero = pm == R(0);
+            if (zero) {
+                zmask |= 1u << jj;
+                if (info == 0) info = j0 + jj + 1;
+            }
+            const T r = O::recip(piv);
+            const bool small = !(pm >= O::sfmin());
+            // rows below the pivot take the update; the others keep their
+            // values (selected, not skipped, so that the whole step stays one
+            // block the scheduler can interleave with the next pivot search)
+            const bool upd = pos > jj && pos < m && !zero;
+            T l = O::mul(a[jj], r);
+            if (__builtin_amdgcn_ballot_w64(small && upd) != 0) {
+                asm volatile("" ::: "memory");
+                if (small && upd) l = O::div(a[jj], piv);
+            }
+            a[jj] = upd ? l : a[jj];
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+                if (c > jj) {
+                    T t = a[c];
+                    O::fms(t, l, u[c]);
+                    a[c] = upd ? t : a[c];
+                }
+        }
+        // rows to their final positions; L11 to LDS for the U12 solve
+        if (tid < m) {
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+                if (c < w) st(M, at(j0 + pos, j0 + c), a[c]);
+            if (pos < w) {   // stored transposed: a column of L11 is contiguous
+#pragma unroll
+                for (int c = 0; c < NB; ++c) l11[c][pos] = a[c];
+            }
+        }
+        if (tid == 0) nlow = 0;
+        lds_barrier();   // the row stores drain behind the next phases
+        if (tid < w) p.ipiv[mat * p.sP + j0 + tid] = sipiv[j0 + tid] + 1;
+        const int rest = n - j0 - w;
+        if (rest <= 0) break;
+
+        // ---- right interchange bookkeeping (positions relative to j0) -----
+        // (a trailing matrix exists, so this panel is full: w == NB)
+        if (tid < NB) {
+            int sp[NB];
+#pragma unroll
+            for (int s2 = 0; s2 < NB; ++s2) sp[s2] = sipiv[j0 + s2] - j0;
+            int x = tid;
+#pragma unroll
+            for (int s2 = NB - 1; s2 >= 0; --s2) x = (x == s2) ? sp[s2] : (x == sp[s2] ? s2 : x);
+            src_top[tid] = x;
+            const int ps = sipiv[j0 + tid] - j0;
+            bool first = ps >= NB;
+#pragma unroll
+            for (int s2 = 0; s2 < NB; ++s2)
+                if (s2 < tid && sp[s2] == ps) first = false;
+            if (first) {
+                int y = ps;
+#pragma unroll
+                for (int s2 = NB - 1; s2 >= 0; --s2) y = (y == s2) ? sp[s2] : (y == sp[s2] ? s2 : y);
+                const int slot = atomicAdd(&nlow, 1);
+                dst_low[slot] = ps;
+                src_low[slot] = y;
+            }
+        }
+        lds_barrier();
+
+        // ---- trailing columns, in chunks of CW (the LDS stage) ------------
+        const uint32_t Lo = at(j0 + w, j0);
+        for (int c0 = 0; c0 < rest; c0 += CW) {
+            const int cw = min(CW, rest - c0);
+            const int cb = j0 + w + c0;          // first column of the chunk
+            // ---- U12 = L11^-1 (P A12) -----------------------------------------
+            // (1) the new top rows into the LDS stage, 32 lanes down each column
+            for (int e = tid; e < NB * cw; e += NT) {
+                const int f = e % NB, c = e / NB;
+                S[f][c] = ld(M, tag, at(j0 + src_top[f], cb + c));
+            }
+            lds_barrier();
+            // (2) displaced rows: old top rows (not yet overwritten) to their
+            //     new places below (already consumed by (1)); 32 lanes per
+            //     column (one per moved row), loads batched ahead of the
+            //     stores, which never touch a row being read
+            {
+                const int nl = nlow;
+                const int q = tid & (NB - 1);
+                if (q < nl) {
+                    const int srow = j0 + src_low[q], drow = j0 + dst_low[q];
+                    for (int c00 = tid >> 5; c00 < cw; c00 += (NT / NB) * 8) {
+                        T v[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int c = c00 + u * (NT / NB);
+                            v[u] = ld(M, tag, at(srow, cb + (c < cw ? c : 0)));
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int c = c00 + u * (NT / NB);
+                            if (c < cw) st(M, at(drow, cb + c), v[u]);
+                        }
+                    }
+                }
+            }
+            // (3) one thread per column solves with L11 (ascending m)
+            if (tid < cw) {
+                if (zmask == 0) {
+                    T x[NB];
+#pragma unroll
+                    for (int f = 0; f < NB; ++f) x[f] = S[f][tid];
+#pragma unroll
+                    for (int mm = 0; mm < NB; ++mm) {
+#pragma unroll
+                        for (int f = 0; f < NB; ++f)
+                            if (f > mm) O::fms(x[f], l11[mm][f], x[mm]);
+                        __builtin_amdgcn_sched_barrier(0);   // one column of L11 in flight at a time
+                    }
+#pragma unroll
+                    for (int f = 0; f < NB; ++f) S[f][tid] = x[f];
+                } else {
+                    // a zero pivot: its column of L11 is left out (rare; in LDS)
+#pragma unroll 1
+                    for (int mm = 0; mm < NB; ++mm) {
+                        if ((zmask >> mm) & 1u) continue;
+                        const T xm = S[mm][tid];
+#pragma unroll 1
+                        for (int f = mm + 1; f < NB; ++f) {
+                            T v = S[f][tid];
+                            O::fms(v, l11[mm][f], xm);
+                            S[f][tid] = v;
+                        }
+                    }
+                }
+            }
+            __syncthreads();   // the moved rows, the stage and L21 visible to all
+            // (4) U12 to the top rows, down each column
+            for (int e = tid; e < NB * cw; e += NT) {
+                const int f = e % NB, c = e / NB;
+                st(M, at(j0 + f, cb + c), S[f][c]);
+            }
+
+            // ---- A22[:, chunk] -= L21 U12[:, chunk] ------------------------
+            const uint32_t Co = at(j0 + w, cb);
+            if (zmask == 0) {
+                // computed as C^T += U12^T (-L21)^T so that an output register
+                // holds 16 consecutive rows of one column (coalesced C traffic)
+                const int nb = (cw + 15) / 16;
+                const int li = lane & 15, lk = lane >> 4;
+                constexpr int RBP = 2;                   // row blocks per pass
+                constexpr int PASSES = NT / 16 / NW / RBP;
+#pragma unroll 1
+                for (int pass = 0; pass < PASSES; ++pass) {
+                    const int rb0 = (wave + NW * pass * RBP) * 16;
+                    if (rb0 >= rest) continue;
+                    T lv[RBP][NB / 4];
+#pragma unroll
+                    for (int t = 0; t < RBP; ++t) {
+                        const int i = rb0 + NW * 16 * t + li;
+#pragma unroll
+                        for (int s = 0; s < NB / 4; ++s) lv[t][s] = -ld(M, tag, Lo + at(i, 4 * s + lk));
+                    }
+                    // C tiles of the next column block are loaded while the
+                    // current one runs on the matrix cores
+                    auto load_c = [&](int bj, V (&cc)[RBP]) {
+#pragma unroll
+                        for (int t = 0; t < RBP; ++t)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                cc[t][r] = ld(M, tag, Co + at(rb0 + NW * 16 * t + li, bj * 16 + mfma_row<T>(lk, r)));
+                    };
+                    V cc[RBP];
+                    load_c(0, cc);
+#pragma unroll 1
+                    for (int bj = 0; bj < nb; ++bj) {
+                        // out-of-range rows and columns read harmless values (or
+                        // 0 past the extent); they only reach outputs not stored
+                        const int j = bj * 16 + li;
+                        T uv[NB / 4];
+#pragma unroll
+                        for (int s = 0; s < NB / 4; ++s) uv[s] = S[4 * s + lk][j < SLD ? j : 0];
+                        V cn[RBP];
+                        load_c(bj + 1 < nb ? bj + 1 : bj, cn);
+#pragma unroll
+                        for (int t = 0; t < RBP; ++t) {
+                            const int i = rb0 + NW * 16 * t + li;
+                            if (rb0 + NW * 16 * t >= rest) continue;
+                            V acc = cc[t];
+#pragma unroll
+                            for (int s = 0; s < NB / 4; ++s) {
+                                if constexpr (sizeof(T) == 4)
+                                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(uv[s], lv[t][s], acc, 0, 0, 0);
+                                else
+                                    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(uv[s], lv[t][s], acc, 0, 0, 0);
+                            }
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int jc = bj * 16 + mfma_row<T>(lk, r);
+                                if (i < rest && jc < cw) st(M, Co + at(i, jc), (T)acc[r]);
+                            }
+                        }
+#pragma unroll
+                        for (int t = 0; t < RBP; ++t) cc[t] = cn[t];
+                    }
+                }
+            } else {
+                // a zero pivot in this panel: leave its k out (rare; VALU)
+#pragma unroll 1
+                for (int e = tid; e < rest * cw; e += NT) {
+                    const int i = e % rest, j = e / rest;
+                    T c = ld(M, tag, Co + at(i, j));
+#pragma unroll 1
+                    for (int k = 0; k < NB; ++k)
+                        if (!((zmask >> k) & 1u)) O::fms(c, ld(M, tag, Lo + at(i, k)), S[k][j]);
+                    st(M, Co + at(i, j), c);
+                }
+            }
+            lds_barrier();   // the stage is refilled by the next chunk
+        }
+        __syncthreads();
+    }
+
+    // ---- deferred left interchange ------------------------------------------
+    const int tid = tid0;
+    const int P = (n + NB - 1) / NB;
+    int map = tid;
+    for (int k = P - 2; k >= 0; --k) {
+        const int lo = (k + 1) * NB;
+        const int hi = min(n, lo + NB);
+        if (tid >= lo && tid < n)
+            for (int s = hi - 1; s >= lo; --s) {
+                const int ps = sipiv[s];
+                map = (map == s) ? ps : (map == ps ? s : map);
+            }
+        const bool mv = tid >= lo && tid < n && map != tid;
+        T v[NB];
+        if (mv) {
+#pragma unroll
+            for (int c = 0; c < NB; ++c) v[c] = ld(M, tag, at(map, k * NB + c));
+        }
+        __syncthreads();
+        if (mv) {
+#pragma unroll
+            for (int c = 0; c < NB; ++c) st(M, at(tid, k * NB + c), v[c]);
+        }
+        __syncthreads();
+    }
+    if (tid == 0) p.info[mat] = info;
+}
+
+}  // namespace
+
+// bytes from a matrix's first element to one past its last
+static long long extent_of(int dtype, int n, int lda) {
+    return ((long long)(n - 1) * lda + n) * elem_bytes(dtype);
+}
+
+bool blocked_fused_supported(int dtype, int n, int lda) {
+    return (dtype == R32 || dtype == R64) && n >= 1 && n <= NT && extent_of(dtype, n, lda) < (1ll << 31);
+}
+
+hipError_t blocked_fused_getrf(int dtype, const Problem& p, hipStream_t s) {
+    if (!blocked_fused_supported(dtype, p.n, p.lda)) return hipErrorInvalidValue;
+    const uint32_t ext = (uint32_t)extent_of(dtype, p.n, p.lda);
+    if (dtype == R32)
+        hipLaunchKernelGGL((lu_fused_kernel<float, 4>), dim3((unsigned)p.batch), dim3(NT), 0, s, p, ext);
+    else
+        hipLaunchKernelGGL((lu_fused_kernel<double, 2>), dim3((unsigned)p.batch), dim3(NT), 0, s, p, ext);
+    return hipGetLastError();
+}
+
+}  // namespace batchlu

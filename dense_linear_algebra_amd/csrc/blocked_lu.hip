@@ -660,6 +660,8 @@ bool blocked_supported(int dtype, int n) {
 
 hipError_t blocked_getrf(int dtype, const Problem& p, hipStream_t s) {
     if (!blocked_supported(dtype, p.n)) return hipErrorInvalidValue;
+    // real orders up to 256: the whole blocked sequence in one work-group
+    if (blocked_fused_supported(dtype, p.n, p.lda)) return blocked_fused_getrf(dtype, p, s);
     switch (dtype) {
     case R32: return getrf_t<float>(p, s);
     case R64: return getrf_t<double>(p, s);

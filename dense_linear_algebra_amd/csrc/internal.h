@@ -33,6 +33,10 @@ hipError_t register_launch(int dtype, const Problem& p, int mode, bool one_wave_
 bool getrs_rows_supported(int dtype, int n);
 hipError_t getrs_rows_launch(int dtype, const Problem& p, hipStream_t s);
 
+// Blocked tier in one work-group per matrix (real types, n <= 256).
+bool blocked_fused_supported(int dtype, int n, int lda);
+hipError_t blocked_fused_getrf(int dtype, const Problem& p, hipStream_t s);
+
 // Blocked right-looking tier (panel, laswp, trsm, gemm) and blocked getrs.
 bool blocked_supported(int dtype, int n);
 hipError_t blocked_getrf(int dtype, const Problem& p, hipStream_t s);
