@@ -75,73 +75,11 @@ __device__ inline void st(const Buf& b, uint32_t e, double v) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), b.r, (int)(e * 8u), 0, 0);
 }
 
-// work-group barrier that orders LDS only: global stores still in flight are
-// not waited for (used where the next phase reads nothing those stores write)
-__device__ inline void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // row inside a 16x16 MFMA output block held by (lane group lk, register r)
 template <typename T>
 __device__ inline int mfma_row(int lk, int r) {
     return sizeof(T) == 4 ? 4 * lk + r : lk + 4 * r;
 }
-
-// maximum over the wavefront, returned wave-uniform: DPP inside each row of
-// 16 lanes, then the four row results by readlane
-__device__ inline uint32_t wave_max(uint32_t v) {
-    v = group_max<16>(v);
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
-    return a > b ? a : b;
-}
-// 64-bit keys: the high words first, then the low words among the lanes
-// that hold the maximal high word
-__device__ inline uint64_t wave_max(uint64_t v) {
-    const uint32_t hi = (uint32_t)(v >> 32);
-    const uint32_t mh = wave_max(hi);
-    const uint32_t ml = wave_max(hi == mh ? (uint32_t)v : 0u);
-    return ((uint64_t)mh << 32) | ml;
-}
-
-// argmax over the wavefront: the maximal key (wave-uniform) and the lane that
-// holds it, the lowest position winning among equal keys; win = -1 when no
-// lane holds a candidate (every key 0)
-__device__ inline void tie_break(bool at_max, int pos, int& win) {
-    const int q = group_min<64>(at_max ? pos : 0x7fffffff);
-    win = __builtin_ctzll(__builtin_amdgcn_ballot_w64(pos == q));
-}
-__device__ inline void wave_argmax(uint32_t key, int pos, uint32_t& kmax, int& win) {
-    kmax = wave_max(key);
-    win = -1;
-    if (kmax == 0) return;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(key == kmax);
-    win = __builtin_ctzll(hit);
-    if (__builtin_popcountll(hit) != 1) tie_break(key == kmax, pos, win);
-}
-// 64-bit keys: the high words decide unless several lanes share the maximal
-// high word; only then are the low words reduced
-__device__ inline void wave_argmax(uint64_t key, int pos, uint64_t& kmax, int& win) {
-    const uint32_t hi = (uint32_t)(key >> 32);
-    const uint32_t mh = wave_max(hi);
-    uint64_t hit = __builtin_amdgcn_ballot_w64(hi == mh);
-    win = -1;
-    if (mh != 0 && __builtin_popcountll(hit) == 1) {
-        win = __builtin_ctzll(hit);
-        kmax = ((uint64_t)mh << 32) | (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, win);
-        return;
-    }
-    const uint32_t ml = wave_max(hi == mh ? (uint32_t)key : 0u);
-    kmax = ((uint64_t)mh << 32) | ml;
-    if (kmax == 0) return;
-    hit = __builtin_amdgcn_ballot_w64(key == kmax);
-    win = __builtin_ctzll(hit);
-    if (__builtin_popcountll(hit) != 1) tie_break(key == kmax, pos, win);
-}
-
 
 // WPE: wavefronts per SIMD the registers are budgeted for (= work-groups per
 // compute unit: f32 4; f64 2, which its LDS stage allows as well)

@@ -158,6 +158,171 @@ __global__ void __launch_bounds__(MAXT) panel_kernel(Problem p, int j0, int w)
     }
 }
 
+// Four wavefronts, RPT rows per thread (row = tid + 256 q), ONE work-group
+// barrier per column: each wavefront finds its argmax (rows of a lane first,
+// then DPP and readlane across lanes) and publishes key, position and
+// candidate row to a double-buffered LDS slot; every thread reads the four
+// slots and picks the winner.  Fewer, fuller wavefronts than one row per
+// thread: the per-step overhead (reduction, exchange, reciprocal) is paid by
+// four wavefronts instead of up to sixteen.
+template <typename T, int RPT>
+__global__ void __launch_bounds__(256) panel4_kernel(Problem p, int j0, int w)
+{
+    using O = ops<T>;
+    using R = typename O::R;
+    using K = typename O::K;
+    constexpr int NT = 256, NW = 4;
+    const int m = p.n - j0;                 // panel height
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const long long mat = blockIdx.x;
+
+    __shared__ K skey[2][NW];
+    __shared__ int spos[2][NW];
+    __shared__ __attribute__((aligned(16))) T cand[2][NW][NBP];
+    __shared__ int srec[NBP];
+
+    T* A = (T*)p.A + mat * p.sA + j0 + (long long)j0 * p.lda;   // panel origin
+
+    T a[RPT][NBP];
+    int pos[RPT];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+        const int r = tid + q * NT;
+        pos[q] = r < m ? r : 0x3fffffff;
+#pragma unroll
+        for (int c = 0; c < NBP; ++c) a[q][c] = (r < m && c < w) ? A[r + (long long)c * p.lda] : O::zero();
+    }
+
+    int info = 0;
+#pragma unroll
+    for (int jj = 0; jj < NBP; ++jj) {
+        if (jj >= w) continue;
+        const int buf = jj & 1;
+        // a1: the lane's best row (lowest position among equal keys), then
+        // the wavefront's
+        K key = 0;
+        int kp = 0x7fffffff, ks = 0;
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            const K kq = (pos[q] >= jj && pos[q] < m) ? (K)pivot_key(O::metric(a[q][jj])) : (K)0;
+            const bool take = kq > key || (kq == key && pos[q] < kp);
+            key = take ? kq : key;
+            kp = take ? pos[q] : kp;
+            ks = take ? q : ks;
+        }
+        K kmax;
+        int win;
+        wave_argmax(key, kp, kmax, win);
+        if (win < 0) {
+            if (lane == 0) {
+                skey[buf][wave] = 0;
+                spos[buf][wave] = 0x7fffffff;
+            }
+        } else if (lane == win) {
+            skey[buf][wave] = kmax;
+            spos[buf][wave] = kp;
+#pragma unroll
+            for (int q = 0; q < RPT; ++q) {
+                if (q != ks) continue;
+                if constexpr (O::is_complex) {
+#pragma unroll
+                    for (int c = 0; c < NBP; ++c)
+                        if (c >= jj) cand[buf][wave][c] = a[q][c];
+                } else {
+                    // 16-byte pieces from the piece holding column jj on
+                    typedef T vec_t __attribute__((ext_vector_type(16 / sizeof(T))));
+                    constexpr int E = 16 / sizeof(T);
+#pragma unroll
+                    for (int c = 0; c < NBP; c += E) {
+                        if (c + E <= jj) continue;
+                        vec_t v;
+#pragma unroll
+                        for (int e = 0; e < E; ++e) v[e] = a[q][c + e];
+                        *(vec_t*)&cand[buf][wave][c] = v;
+                    }
+                }
+            }
+        }
+        lds_barrier();
+        K kv[NW];
+        int pv[NW];
+        T cv[NW];
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            kv[v] = skey[buf][v];
+            pv[v] = spos[buf][v];
+            cv[v] = cand[buf][v][jj];
+        }
+        K best = kv[0];
+        int ppos = pv[0], vb = 0;
+        T piv = cv[0];
+#pragma unroll
+        for (int v = 1; v < NW; ++v) {
+            const bool take = kv[v] > best || (kv[v] == best && pv[v] < ppos);
+            best = take ? kv[v] : best;
+            ppos = take ? pv[v] : ppos;
+            vb = take ? v : vb;
+            piv = take ? cv[v] : piv;
+        }
+        // the pivot row through one VGPR base and immediate offsets
+        typedef __attribute__((address_space(3))) const T lds_t;
+        uint32_t rowaddr = (uint32_t)(uintptr_t)(lds_t*)&cand[buf][vb][0];
+        asm volatile("" : "+v"(rowaddr));
+        lds_t* row = (lds_t*)(uintptr_t)rowaddr;
+        T u[NBP];
+#pragma unroll
+        for (int c = 0; c < NBP; ++c) {
+            if constexpr (O::is_complex) {
+                if (c > jj) u[c] = cand[buf][vb][c];
+            } else {
+                if (c > jj) u[c] = row[c];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            if (pos[q] == ppos) srec[jj] = ppos;   // the pivot row's owner records it
+            pos[q] = (pos[q] == ppos) ? jj : (pos[q] == jj ? ppos : pos[q]);
+        }
+        const R pm = O::metric(piv);
+        const bool zero = pm == R(0);
+        if (zero && info == 0) info = j0 + jj + 1;
+        const T r = O::recip(piv);
+        const bool small = !(pm >= O::sfmin());
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            if (pos[q] > jj && pos[q] < m && !zero) {
+                T l = O::mul(a[q][jj], r);
+                if (__builtin_amdgcn_ballot_w64(small) != 0) {
+                    asm volatile("" ::: "memory");
+                    if (small) l = O::div(a[q][jj], piv);
+                }
+                a[q][jj] = l;
+#pragma unroll
+                for (int c = 0; c < NBP; ++c)
+                    if (c > jj) O::fms(a[q][c], l, u[c]);
+            }
+        }
+    }
+    __syncthreads();
+    // rows to their final positions; ipiv as global 1-based rows
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+        const int r = tid + q * NT;
+        if (r < m)
+#pragma unroll
+            for (int c = 0; c < NBP; ++c)
+                if (c < w) A[pos[q] + (long long)c * p.lda] = a[q][c];
+    }
+    if (tid < w) p.ipiv[mat * p.sP + j0 + tid] = j0 + srec[tid] + 1;
+    if (tid == 0) {
+        int* ip = p.info + mat;
+        if (j0 == 0) *ip = info;
+        else if (info != 0 && *ip == 0) *ip = info;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // interchange bookkeeping shared by the right-swap solve: destination rows
 // of the panel's transpositions and the source row of each (a backward trace
@@ -260,6 +425,11 @@ __global__ void __launch_bounds__(64) trsm_block_kernel(const void* Tmat, int ld
 // multiply-add per k in that order.
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// row inside a 16x16 MFMA output block held by (lane group lk, register r)
+template <typename T>
+__device__ inline int mfma_row_t(int lk, int r) {
+    return sizeof(T) == 4 ? 4 * lk + r : lk + 4 * r;
+}
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
@@ -284,6 +454,130 @@ __device__ inline void tile_load(T (*As)[TT], T (*Bs)[TT], const T* Ap, int lda_
 
 // MFMA version for float and double: 4 waves, each a 32 x 32 quarter of the
 // 64 x 64 tile made of 2 x 2 blocks of 16 x 16.
+// U12 = L11^-1 (P A12) for the getrf trailing columns, through an LDS stage:
+// the new top rows are gathered 32 lanes down each column (coalesced), the
+// displaced rows move with one lane per moved row, one thread per column
+// solves with L11 from LDS (ascending m; a zero pivot's column is left out,
+// as in the unblocked order), and the stage is written back down each column.
+template <typename T>
+struct StageTile {
+    static constexpr int TC = sizeof(T) == 4 ? 256 : (sizeof(T) == 8 ? 128 : 64);   // columns per work-group
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) trsm_stage_kernel(Problem p, int r0, int ncols, int ctiles)
+{
+    using O = ops<T>;
+    using R = typename O::R;
+    constexpr int NT = 256;
+    constexpr int TC = StageTile<T>::TC;
+    __shared__ T S[NBP][TC + 1];
+    __shared__ T l11[NBP][NBP];              // transposed: l11[m][f] = l_fm
+    __shared__ int src_top[NBP], src_low[NBP], dst_low[NBP];
+    __shared__ int nlow;
+    __shared__ unsigned zmask;
+    const int tid = threadIdx.x;
+    const long long mat = blockIdx.x / ctiles;
+    const int c0 = (int)(blockIdx.x % ctiles) * TC;
+    const int ct = min(TC, ncols - c0);
+    const long long lda = p.lda;
+    T* A = (T*)p.A + mat * p.sA;
+    T* X = A + r0 + (long long)(r0 + NBP + c0) * lda;        // top-left of this tile's P A12 block
+    const T* D = A + r0 + (long long)r0 * lda;                // L11 / U11 block
+    if (tid == 0) {
+        nlow = 0;
+        zmask = 0;
+    }
+    for (int e = tid; e < NBP * NBP; e += NT) {
+        const int f = e % NBP, mm = e / NBP;
+        l11[mm][f] = D[f + mm * lda];
+    }
+    __syncthreads();
+    if (tid < NBP) {
+        int sp[NBP];
+#pragma unroll
+        for (int s2 = 0; s2 < NBP; ++s2) sp[s2] = p.ipiv[mat * p.sP + r0 + s2] - 1 - r0;
+        int x = tid;
+#pragma unroll
+        for (int s2 = NBP - 1; s2 >= 0; --s2) x = (x == s2) ? sp[s2] : (x == sp[s2] ? s2 : x);
+        src_top[tid] = x;
+        const int ps = p.ipiv[mat * p.sP + r0 + tid] - 1 - r0;
+        bool first = ps >= NBP;
+#pragma unroll
+        for (int s2 = 0; s2 < NBP; ++s2)
+            if (s2 < tid && sp[s2] == ps) first = false;
+        if (first) {
+            int y = ps;
+#pragma unroll
+            for (int s2 = NBP - 1; s2 >= 0; --s2) y = (y == s2) ? sp[s2] : (y == sp[s2] ? s2 : y);
+            const int slot = atomicAdd(&nlow, 1);
+            dst_low[slot] = ps;
+            src_low[slot] = y;
+        }
+        if (O::metric(l11[tid][tid]) == R(0)) atomicOr(&zmask, 1u << tid);
+    }
+    __syncthreads();
+    // (1) the new top rows into the stage
+    for (int e = tid; e < NBP * ct; e += NT) {
+        const int f = e % NBP, c = e / NBP;
+        S[f][c] = X[src_top[f] + (long long)c * lda];
+    }
+    __syncthreads();
+    // (2) displaced rows: old top rows to their new places below
+    {
+        const int nl = nlow;
+        const int q = tid & (NBP - 1);
+        if (q < nl) {
+            const int srow = src_low[q], drow = dst_low[q];
+            for (int c00 = tid >> 5; c00 < ct; c00 += (NT / NBP) * 8) {
+                T v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int c = c00 + u * (NT / NBP);
+                    if (c < ct) v[u] = X[srow + (long long)c * lda];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int c = c00 + u * (NT / NBP);
+                    if (c < ct) X[drow + (long long)c * lda] = v[u];
+                }
+            }
+        }
+    }
+    // (3) one thread per column
+    const unsigned zm = zmask;
+    if (tid < ct) {
+        T x[NBP];
+#pragma unroll
+        for (int f = 0; f < NBP; ++f) x[f] = S[f][tid];
+        if (zm == 0) {
+#pragma unroll
+            for (int mm = 0; mm < NBP; ++mm) {
+#pragma unroll
+                for (int f = 0; f < NBP; ++f)
+                    if (f > mm) O::fms(x[f], l11[mm][f], x[mm]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int mm = 0; mm < NBP; ++mm) {
+                const bool skip = (zm >> mm) & 1u;
+#pragma unroll
+                for (int f = 0; f < NBP; ++f)
+                    if (f > mm && !skip) O::fms(x[f], l11[mm][f], x[mm]);
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < NBP; ++f) S[f][tid] = x[f];
+    }
+    __syncthreads();
+    // (4) U12 down each column
+    for (int e = tid; e < NBP * ct; e += NT) {
+        const int f = e % NBP, c = e / NBP;
+        X[f + (long long)c * lda] = S[f][c];
+    }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) gemm_mfma_kernel(const void* Am, int lda_, long long sA, const void* Bm,
                                                         int ldb_, long long sB, void* Cm, int ldc, long long sC,
@@ -364,6 +658,139 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const void* Am, int lda_
                 const int j = wc + bj * 16 + li;
                 if (i < Mt && j < Nt) Cp[i + (long long)j * ldc] = acc[bi][bj][r];
             }
+}
+
+// getrf trailing update A22 -= L21 U12 (real types, K = 32, ascending k): one
+// work-group per 64-row strip of one matrix walks the strip's 64-column
+// tiles.  L21 stays in registers as MFMA operands for the whole strip; the
+// next U12 tile is staged into LDS and the next C tile loaded while the
+// current one runs on the matrix cores.  Computed as C^T += U12^T (-L21)^T so
+// that an accumulator register holds 16 consecutive rows of one column.  A
+// zero pivot among the panel's 32 (a zero diagonal entry of U11) leaves its
+// k out, on the VALU, as in the unblocked order.
+template <typename T>
+__global__ void __launch_bounds__(256) update_strip_kernel(T* A, int lda, long long sA, int j0, int M, int mstrips)
+{
+    using O = ops<T>;
+    using R = typename O::R;
+    using V = typename std::conditional<sizeof(T) == 4, f32x4, f64x4>::type;
+    constexpr int UP = 64 + (sizeof(T) == 4 ? 4 : 2);       // padded row of the U tile
+    __shared__ __attribute__((aligned(16))) T Us[2][NBP][UP];
+    __shared__ unsigned zmask;
+    const int tid = threadIdx.x;
+    const long long mat = blockIdx.x / mstrips;
+    const int r0 = (int)(blockIdx.x % mstrips) * 64;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wr = wave & 1, wc = wave >> 1;
+    const int li = lane & 15, lk = lane >> 4;
+    T* base = A + mat * sA;
+    const T* Lp = base + j0 + NBP + (long long)j0 * lda;             // L21
+    const T* Up = base + j0 + (long long)(j0 + NBP) * lda;           // U12
+    T* Cp = base + j0 + NBP + (long long)(j0 + NBP) * lda;           // A22
+    const int N = M;
+    const int nct = (N + 63) / 64;
+    if (tid == 0) zmask = 0;
+    __syncthreads();
+    if (tid < NBP && O::metric(base[j0 + tid + (long long)(j0 + tid) * lda]) == R(0)) atomicOr(&zmask, 1u << tid);
+    // the first U tile into the stage
+    auto load_u = [&](int ct, T (&v)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = tid + 256 * u, k = e & (NBP - 1), c = ct * 64 + (e >> 5);
+            v[u] = c < N ? Up[k + (long long)c * lda] : O::zero();
+        }
+    };
+    auto put_u = [&](int b, const T (&v)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = tid + 256 * u;
+            Us[b][e & (NBP - 1)][e >> 5] = v[u];
+        }
+    };
+    {
+        T v[8];
+        load_u(0, v);
+        put_u(0, v);
+    }
+    __syncthreads();
+    if (zmask != 0) {
+        // a zero pivot in this panel: plain k loop without that k (rare)
+#pragma unroll 1
+        for (int e = tid; e < 64 * N; e += 256) {
+            const int i = r0 + (e & 63), j = e >> 6;
+            if (i >= M) continue;
+            T c = Cp[i + (long long)j * lda];
+#pragma unroll 1
+            for (int k = 0; k < NBP; ++k)
+                if (!((zmask >> k) & 1u)) O::fms(c, Lp[i + (long long)k * lda], Up[k + (long long)j * lda]);
+            Cp[i + (long long)j * lda] = c;
+        }
+        return;
+    }
+    // L21 operands of this wavefront's two 16-row blocks, negated
+    T lv[2][NBP / 4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int i = r0 + wr * 32 + t * 16 + li;
+#pragma unroll
+        for (int s2 = 0; s2 < NBP / 4; ++s2) lv[t][s2] = i < M ? -Lp[i + (long long)(4 * s2 + lk) * lda] : O::zero();
+    }
+    auto load_c = [&](int ct, V (&c)[2][2]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = r0 + wr * 32 + t * 16 + li;
+                    const int j = ct * 64 + wc * 32 + b * 16 + mfma_row_t<T>(lk, r);
+                    c[t][b][r] = (i < M && j < N) ? Cp[i + (long long)j * lda] : O::zero();
+                }
+    };
+    V cc[2][2];
+    load_c(0, cc);
+#pragma unroll 1
+    for (int ct = 0; ct < nct; ++ct) {
+        const int buf = ct & 1;
+        T un[8];
+        V cn[2][2];
+        const bool more = ct + 1 < nct;
+        if (more) {
+            load_u(ct + 1, un);
+            load_c(ct + 1, cn);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            T uv[NBP / 4];
+#pragma unroll
+            for (int s2 = 0; s2 < NBP / 4; ++s2) uv[s2] = Us[buf][4 * s2 + lk][wc * 32 + b * 16 + li];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                V acc = cc[t][b];
+#pragma unroll
+                for (int s2 = 0; s2 < NBP / 4; ++s2) {
+                    if constexpr (sizeof(T) == 4)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(uv[s2], lv[t][s2], acc, 0, 0, 0);
+                    else
+                        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(uv[s2], lv[t][s2], acc, 0, 0, 0);
+                }
+                const int i = r0 + wr * 32 + t * 16 + li;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = ct * 64 + wc * 32 + b * 16 + mfma_row_t<T>(lk, r);
+                    if (i < M && j < N) Cp[i + (long long)j * lda] = acc[r];
+                }
+            }
+        }
+        if (more) {
+            put_u(buf ^ 1, un);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) cc[t][b] = cn[t][b];
+        }
+        __syncthreads();
+    }
 }
 
 // VALU version (complex types): each thread owns a 4 x 4 block of the tile.
@@ -529,6 +956,18 @@ template <typename T>
 hipError_t launch_panel(const Problem& p, int j0, int w, hipStream_t s) {
     constexpr int CAP = panel_cap<T>();
     const int m = p.n - j0;
+    // four wavefronts with up to four rows per thread while the rows fit in
+    // registers (real types to 1024 rows, complex float to 512)
+    if constexpr (sizeof(T) <= 8) {
+        constexpr int CAP4 = ops<T>::is_complex ? 512 : 1024;
+        if (m <= CAP4) {
+            if (m <= 256) hipLaunchKernelGGL((panel4_kernel<T, 1>), dim3(p.batch), dim3(256), 0, s, p, j0, w);
+            else if (m <= 512) hipLaunchKernelGGL((panel4_kernel<T, 2>), dim3(p.batch), dim3(256), 0, s, p, j0, w);
+            else if constexpr (!ops<T>::is_complex)
+                hipLaunchKernelGGL((panel4_kernel<T, 4>), dim3(p.batch), dim3(256), 0, s, p, j0, w);
+            return hipGetLastError();
+        }
+    }
     int nt = ((m + 63) / 64) * 64;
     if (nt > CAP) nt = CAP;
     const int rpt = (m + nt - 1) / nt;
@@ -587,16 +1026,31 @@ hipError_t getrf_t(const Problem& p, hipStream_t s) {
         const int rest = n - j0 - w;
         if (rest <= 0) break;
         T* A = (T*)p.A;
-        // U12 = L11^-1 * (P A12), displaced rows moved
-        if ((e = launch_trsm<T>(A, p.lda, p.sA, A + (long long)(j0 + w) * p.lda, p.lda, p.sA, j0, w, rest,
-                                p.batch, p.ipiv, p.sP, true, false, nullptr, s)) != hipSuccess)
-            return e;
+        // U12 = L11^-1 * (P A12), displaced rows moved (w == NBP: a trailing
+        // matrix exists)
+        if constexpr (sizeof(T) <= 8) {
+            constexpr int TC = StageTile<T>::TC;
+            const int ct = (rest + TC - 1) / TC;
+            hipLaunchKernelGGL((trsm_stage_kernel<T>), dim3((unsigned)((long long)ct * p.batch)), dim3(256), 0, s, p,
+                               j0, rest, ct);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        } else {   // complex double: the stage would not fit the registers
+            if ((e = launch_trsm<T>(A, p.lda, p.sA, A + (long long)(j0 + w) * p.lda, p.lda, p.sA, j0, w, rest,
+                                    p.batch, p.ipiv, p.sP, true, false, nullptr, s)) != hipSuccess)
+                return e;
+        }
         // A22 -= L21 * U12
-        if ((e = launch_gemm<T>(A + j0 + w + (long long)j0 * p.lda, p.lda, p.sA,
-                                A + j0 + (long long)(j0 + w) * p.lda, p.lda, p.sA,
-                                A + j0 + w + (long long)(j0 + w) * p.lda, p.lda, p.sA, rest, rest, w, p.batch, 1,
-                                nullptr, s)) != hipSuccess)
+        if constexpr (!ops<T>::is_complex) {
+            const int ms = (rest + 63) / 64;
+            hipLaunchKernelGGL((update_strip_kernel<T>), dim3((unsigned)((long long)ms * p.batch)), dim3(256), 0, s,
+                               A, p.lda, p.sA, j0, rest, ms);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        } else if ((e = launch_gemm<T>(A + j0 + w + (long long)j0 * p.lda, p.lda, p.sA,
+                                       A + j0 + (long long)(j0 + w) * p.lda, p.lda, p.sA,
+                                       A + j0 + w + (long long)(j0 + w) * p.lda, p.lda, p.sA, rest, rest, w, p.batch,
+                                       1, nullptr, s)) != hipSuccess) {
             return e;
+        }
     }
     if (n > NBP) {
         const int nt = panel_threads(n);

@@ -194,12 +194,15 @@ bool getrs_rows_supported(int dtype, int n) {
 
 hipError_t getrs_rows_launch(int dtype, const Problem& p, hipStream_t s) {
     if (!getrs_rows_supported(dtype, p.n)) return hipErrorInvalidValue;
-    const bool one = p.nrhs <= 1;
+    // right-hand sides per work-group (each group streams all of L and U;
+    // wider tiles were measured slower at n = 1024, nrhs = 32: fewer groups)
+    const int r = p.nrhs;
     switch (dtype) {
-    case R32: return one ? launch_t<float, 1>(p, s) : launch_t<float, 4>(p, s);
-    case R64: return one ? launch_t<double, 1>(p, s) : launch_t<double, 4>(p, s);
-    case C64: return one ? launch_t<cplx<float>, 1>(p, s) : launch_t<cplx<float>, 2>(p, s);
-    case C128: return launch_t<cplx<double>, 1>(p, s);
+    case R32: return r <= 1 ? launch_t<float, 1>(p, s) : launch_t<float, 4>(p, s);
+    case R64: return r <= 1 ? launch_t<double, 1>(p, s) : launch_t<double, 4>(p, s);
+    case C64: return r <= 1 ? launch_t<cplx<float>, 1>(p, s) : r <= 2 ? launch_t<cplx<float>, 2>(p, s)
+                                                              : launch_t<cplx<float>, 4>(p, s);
+    case C128: return r <= 1 ? launch_t<cplx<double>, 1>(p, s) : launch_t<cplx<double>, 2>(p, s);
     default: return hipErrorInvalidValue;
     }
 }

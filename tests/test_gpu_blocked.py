@@ -31,8 +31,8 @@ def _blocked_tier():
     lib.batchlu_set_tier(lib.TIER_AUTO)
 
 
-CASES = ([(np.float32, n) for n in (1, 7, 32, 33, 64, 65, 100, 161, 256)]
-         + [(np.float64, n) for n in (31, 64, 96, 130, 256)]
+CASES = ([(np.float32, n) for n in (1, 7, 32, 33, 64, 65, 100, 161, 256, 290, 520)]
+         + [(np.float64, n) for n in (31, 64, 96, 130, 256, 300)]
          + [(np.complex64, n) for n in (40, 64, 100)]
          + [(np.complex128, n) for n in (33, 70)])
 
@@ -95,12 +95,14 @@ def _one(M, dtype):
     return np.ascontiguousarray(np.asarray(M, dtype=dtype).T).reshape(-1).copy()
 
 
+@pytest.mark.parametrize("n", [90, 300])
 @pytest.mark.parametrize("dtype", [np.float32, np.float64, np.complex64])
-def test_blocked_special_matrices(dtype):
-    """Wilkinson growth across three panels (every step a tie), a zero column
-    inside the second panel (info from a later panel), a singular last step
-    and a NaN; B untouched where info > 0."""
-    n, nrhs = 90, 2
+def test_blocked_special_matrices(dtype, n):
+    """Wilkinson growth across several panels (every step a tie), a zero
+    column inside the second panel (info from a later panel), a singular last
+    step and a NaN; B untouched where info > 0.  n = 90 runs the one-work-group
+    kernel for real types, n = 300 the multi-launch sequence."""
+    nrhs = 2
     rng = np.random.default_rng(3)
     W = np.tril(-np.ones((n, n)), -1) + np.eye(n)
     W[:, -1] = 1
