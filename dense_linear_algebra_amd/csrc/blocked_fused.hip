@@ -14,8 +14,10 @@
 //           double-buffered LDS slot; every thread then reads the four
 //           slots in one round trip and picks the winner;
 //   right   the panel's transpositions reach the trailing columns as one
-//           gather of the new top rows into an LDS stage plus the displaced
-//           rows' moves;
+//           gather of the new top rows into an LDS stage; a displaced row is
+//           read by the update from the old top row that moves there (the
+//           update writes every trailing row anyway), and U12 replaces the
+//           top rows only after the update has read them;
 //   U12     one thread per trailing column solves in the LDS stage,
 //           ascending m, L11 from LDS; the stage then feeds the update and
 //           is written back down each column;
@@ -100,6 +102,7 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
     __shared__ int sipiv[NT];                 // pivot rows, 0-based, global
     __shared__ int src_top[NB], src_low[NB], dst_low[NB];
     __shared__ int nlow;
+    __shared__ int csrc[NT];                  // trailing position -> row holding it (relative to j0)
     constexpr int CW = Stage<T>::CW, SLD = Stage<T>::SLD;
     __shared__ T S[NB][SLD];                  // P A12, then U12 (rows of the panel x trailing columns)
 
@@ -257,6 +260,11 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
                 src_low[slot] = y;
             }
         }
+        csrc[tid] = tid;
+        lds_barrier();
+        // a displaced trailing row is read by the update from the old top
+        // row that moves there (the top rows are overwritten only after it)
+        if (tid < nlow) csrc[dst_low[tid]] = src_low[tid];
         lds_barrier();
 
         // ---- trailing columns, in chunks of CW (the LDS stage) ------------
@@ -266,35 +274,20 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
             const int cb = j0 + w + c0;          // first column of the chunk
             // ---- U12 = L11^-1 (P A12) -----------------------------------------
             // (1) the new top rows into the LDS stage, 32 lanes down each column
-            for (int e = tid; e < NB * cw; e += NT) {
-                const int f = e % NB, c = e / NB;
-                S[f][c] = ld(M, tag, at(j0 + src_top[f], cb + c));
-            }
-            lds_barrier();
-            // (2) displaced rows: old top rows (not yet overwritten) to their
-            //     new places below (already consumed by (1)); 32 lanes per
-            //     column (one per moved row), loads batched ahead of the
-            //     stores, which never touch a row being read
-            {
-                const int nl = nlow;
-                const int q = tid & (NB - 1);
-                if (q < nl) {
-                    const int srow = j0 + src_low[q], drow = j0 + dst_low[q];
-                    for (int c00 = tid >> 5; c00 < cw; c00 += (NT / NB) * 8) {
-                        T v[8];
+            for (int e0 = tid; e0 < NB * cw; e0 += NT * 8) {   // loads batched
+                T v[8];
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) {
-                            const int c = c00 + u * (NT / NB);
-                            v[u] = ld(M, tag, at(srow, cb + (c < cw ? c : 0)));
-                        }
+                for (int u = 0; u < 8; ++u) {
+                    const int e = e0 + u * NT;
+                    v[u] = ld(M, tag, at(j0 + src_top[e % NB], cb + (e < NB * cw ? e / NB : 0)));
+                }
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) {
-                            const int c = c00 + u * (NT / NB);
-                            if (c < cw) st(M, at(drow, cb + c), v[u]);
-                        }
-                    }
+                for (int u = 0; u < 8; ++u) {
+                    const int e = e0 + u * NT;
+                    if (e < NB * cw) S[e % NB][e / NB] = v[u];
                 }
             }
+            lds_barrier();
             // (3) one thread per column solves with L11 (ascending m)
             if (tid < cw) {
                 if (zmask == 0) {
@@ -325,12 +318,7 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
                     }
                 }
             }
-            __syncthreads();   // the moved rows, the stage and L21 visible to all
-            // (4) U12 to the top rows, down each column
-            for (int e = tid; e < NB * cw; e += NT) {
-                const int f = e % NB, c = e / NB;
-                st(M, at(j0 + f, cb + c), S[f][c]);
-            }
+            __syncthreads();   // the stage and L21 visible to all
 
             // ---- A22[:, chunk] -= L21 U12[:, chunk] ------------------------
             const uint32_t Co = at(j0 + w, cb);
@@ -354,12 +342,21 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
                     }
                     // C tiles of the next column block are loaded while the
                     // current one runs on the matrix cores
+                    // the physical rows of this lane's two output rows (a
+                    // displaced position reads its old top row)
+                    int crow[RBP];
+#pragma unroll
+                    for (int t = 0; t < RBP; ++t) {
+                        const int i = rb0 + NW * 16 * t + li;
+                        crow[t] = i < rest ? csrc[w + i] : w + i;
+                    }
+                    const uint32_t Cr = at(j0, cb);   // row j0 of the chunk's first column
                     auto load_c = [&](int bj, V (&cc)[RBP]) {
 #pragma unroll
                         for (int t = 0; t < RBP; ++t)
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
-                                cc[t][r] = ld(M, tag, Co + at(rb0 + NW * 16 * t + li, bj * 16 + mfma_row<T>(lk, r)));
+                                cc[t][r] = ld(M, tag, Cr + at(crow[t], bj * 16 + mfma_row<T>(lk, r)));
                     };
                     V cc[RBP];
                     load_c(0, cc);
@@ -400,12 +397,18 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
 #pragma unroll 1
                 for (int e = tid; e < rest * cw; e += NT) {
                     const int i = e % rest, j = e / rest;
-                    T c = ld(M, tag, Co + at(i, j));
+                    T c = ld(M, tag, at(j0 + csrc[w + i], cb + j));
 #pragma unroll 1
                     for (int k = 0; k < NB; ++k)
                         if (!((zmask >> k) & 1u)) O::fms(c, ld(M, tag, Lo + at(i, k)), S[k][j]);
                     st(M, Co + at(i, j), c);
                 }
+            }
+            __syncthreads();   // every update read of the old top rows is done
+            // (4) U12 to the top rows, down each column
+            for (int e = tid; e < NB * cw; e += NT) {
+                const int f = e % NB, c = e / NB;
+                st(M, at(j0 + f, cb + c), S[f][c]);
             }
             lds_barrier();   // the stage is refilled by the next chunk
         }

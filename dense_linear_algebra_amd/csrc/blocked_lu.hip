@@ -361,9 +361,18 @@ __global__ void __launch_bounds__(64) trsm_block_kernel(const void* Tmat, int ld
     const T* Tp = (const T*)Tmat + mat * sT + r0 + (long long)r0 * ldt;
     T* Xp = (T*)Xmat + mat * sX + r0;
 
-    for (int e = tid; e < w * w; e += 64) {
-        const int i = e % w, k = e / w;
-        tri[i][k] = Tp[i + (long long)k * ldt];
+    for (int e0 = tid; e0 < w * w; e0 += 64 * 8) {   // loads batched
+        T v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * 64;
+            if (e < w * w) v[u] = Tp[(e % w) + (long long)(e / w) * ldt];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * 64;
+            if (e < w * w) tri[e % w][e / w] = v[u];
+        }
     }
     if (swap) {
         if (tid < w) sp[tid] = ipiv[mat * sP + r0 + tid] - 1 - r0;
@@ -437,18 +446,32 @@ __device__ inline void tile_load(T (*As)[TT], T (*Bs)[TT], const T* Ap, int lda_
                                  int M, int N, int K, int tid, int nthr, bool negate)
 {
     using O = ops<T>;
-    for (int e = tid; e < TT * K; e += nthr) {
-        const int i = e % TT, k = e / TT;
-        T v = i < M ? Ap[i + (long long)k * lda_] : O::zero();
-        if (negate) {
-            if constexpr (O::is_complex) { v.re = -v.re; v.im = -v.im; }
-            else v = -v;
+    // loads issued in batches of eight per thread before their LDS stores
+    for (int e0 = tid; e0 < TT * K; e0 += nthr * 8) {
+        T va[8], vb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * nthr;
+            if (e < TT * K) {
+                const int i = e % TT, k = e / TT;
+                va[u] = i < M ? Ap[i + (long long)k * lda_] : O::zero();
+                const int k2 = e % K, j = e / K;
+                vb[u] = j < N ? Bp[k2 + (long long)j * ldb_] : O::zero();
+            }
         }
-        As[k][i] = v;
-    }
-    for (int e = tid; e < TT * K; e += nthr) {
-        const int k = e % K, j = e / K;
-        Bs[k][j] = j < N ? Bp[k + (long long)j * ldb_] : O::zero();
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * nthr;
+            if (e < TT * K) {
+                T v = va[u];
+                if (negate) {
+                    if constexpr (O::is_complex) { v.re = -v.re; v.im = -v.im; }
+                    else v = -v;
+                }
+                As[e / TT][e % TT] = v;
+                Bs[e % K][e / K] = vb[u];
+            }
+        }
     }
 }
 
@@ -459,17 +482,19 @@ __device__ inline void tile_load(T (*As)[TT], T (*Bs)[TT], const T* Ap, int lda_
 // displaced rows move with one lane per moved row, one thread per column
 // solves with L11 from LDS (ascending m; a zero pivot's column is left out,
 // as in the unblocked order), and the stage is written back down each column.
+// One wavefront per 64-column tile: many small work-groups per compute unit
+// overlap each other's memory latency, and the barriers are a wavefront's.
 template <typename T>
 struct StageTile {
-    static constexpr int TC = sizeof(T) == 4 ? 256 : (sizeof(T) == 8 ? 128 : 64);   // columns per work-group
+    static constexpr int TC = 64;   // columns per work-group = threads
 };
 
 template <typename T>
-__global__ void __launch_bounds__(256) trsm_stage_kernel(Problem p, int r0, int ncols, int ctiles)
+__global__ void __launch_bounds__(64) trsm_stage_kernel(Problem p, int r0, int ncols, int ctiles)
 {
     using O = ops<T>;
     using R = typename O::R;
-    constexpr int NT = 256;
+    constexpr int NT = 64;
     constexpr int TC = StageTile<T>::TC;
     __shared__ T S[NBP][TC + 1];
     __shared__ T l11[NBP][NBP];              // transposed: l11[m][f] = l_fm
@@ -488,9 +513,19 @@ __global__ void __launch_bounds__(256) trsm_stage_kernel(Problem p, int r0, int 
         nlow = 0;
         zmask = 0;
     }
-    for (int e = tid; e < NBP * NBP; e += NT) {
-        const int f = e % NBP, mm = e / NBP;
-        l11[mm][f] = D[f + mm * lda];
+    {
+        constexpr int PER = NBP * NBP / NT;   // loads per thread, issued together
+        T v[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + u * NT;
+            v[u] = D[(e % NBP) + (e / NBP) * lda];
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + u * NT;
+            l11[e / NBP][e % NBP] = v[u];
+        }
     }
     __syncthreads();
     if (tid < NBP) {
@@ -517,10 +552,20 @@ __global__ void __launch_bounds__(256) trsm_stage_kernel(Problem p, int r0, int 
         if (O::metric(l11[tid][tid]) == R(0)) atomicOr(&zmask, 1u << tid);
     }
     __syncthreads();
-    // (1) the new top rows into the stage
-    for (int e = tid; e < NBP * ct; e += NT) {
-        const int f = e % NBP, c = e / NBP;
-        S[f][c] = X[src_top[f] + (long long)c * lda];
+    // (1) the new top rows into the stage (loads batched: one round trip
+    //     per eight elements per thread, not one per element)
+    for (int e0 = tid; e0 < NBP * ct; e0 += NT * 8) {
+        T v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * NT;
+            if (e < NBP * ct) v[u] = X[src_top[e % NBP] + (long long)(e / NBP) * lda];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = e0 + u * NT;
+            if (e < NBP * ct) S[e % NBP][e / NBP] = v[u];
+        }
     }
     __syncthreads();
     // (2) displaced rows: old top rows to their new places below
@@ -1031,7 +1076,7 @@ hipError_t getrf_t(const Problem& p, hipStream_t s) {
         if constexpr (sizeof(T) <= 8) {
             constexpr int TC = StageTile<T>::TC;
             const int ct = (rest + TC - 1) / TC;
-            hipLaunchKernelGGL((trsm_stage_kernel<T>), dim3((unsigned)((long long)ct * p.batch)), dim3(256), 0, s, p,
+            hipLaunchKernelGGL((trsm_stage_kernel<T>), dim3((unsigned)((long long)ct * p.batch)), dim3(TC), 0, s, p,
                                j0, rest, ct);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         } else {   // complex double: the stage would not fit the registers
