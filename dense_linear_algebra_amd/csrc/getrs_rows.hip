@@ -21,7 +21,7 @@ namespace batchlu {
 namespace {
 
 constexpr int BS = 32;   // rows per diagonal block
-constexpr int CK = 8;    // columns of L or U loaded per round
+constexpr int CK = 16;   // columns of L or U loaded per round
 
 template <typename T, int NRT>
 __global__ void __launch_bounds__(1024) getrs_rows_kernel(Problem p, int rtiles)
