@@ -43,8 +43,22 @@ struct vecbits<8> { using type = uint2; };
 template <>
 struct vecbits<16> { using type = uint4; };
 
+// Rows of 512 bytes (64 doubles or complex floats, 32 complex doubles) take
+// the pivot row a chunk at a time where the update consumes it instead of
+// holding it whole; the registers are then budgeted for two wavefronts per
+// SIMD wherever that fits without spilling (checked in the compiler's
+// resource report), so that one wavefront's latency overlaps another's work.
+template <typename T, int NB>
+constexpr bool reg_chunked() { return NB * (int)sizeof(T) >= 512; }
+template <typename T, int NB, int NR>
+constexpr int reg_waves() {
+    if (!reg_chunked<T, NB>()) return 1;
+    if (sizeof(T) == 8) return (ops<T>::is_complex || NR <= 8) ? 2 : 1;
+    return NR <= 1 ? 2 : 1;
+}
+
 template <typename T, int NB, int RPL, int NR>
-__global__ void __launch_bounds__(64 * kWavesPerBlock)
+__global__ void __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(reg_waves<T, NB, NR>())))
 register_lu_kernel(Problem p, int mode)
 {
     using O = ops<T>;
@@ -186,22 +200,31 @@ register_lu_kernel(Problem p, int mode)
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+        // the pivot row: held whole in registers, or (when registers are
+        // budgeted for two wavefronts per SIMD) read a chunk at a time where
+        // the update consumes it
+        constexpr bool chunked = reg_chunked<T, NB>();
         T u[NB];
         T ub[NRP];
+        if constexpr (!chunked) {
 #pragma unroll
-        for (int c = 0; c < NBC; ++c) {
-            if (c < j / CH) continue;
-            uint4 w = rowbuf[grp][c];
-            __builtin_memcpy(&u[c * CH], &w, 16);
-        }
-        if constexpr (NRC > 0) {
-            if (solve) {
+            for (int c = 0; c < NBC; ++c) {
+                if (c < j / CH) continue;
+                uint4 w = rowbuf[grp][c];
+                __builtin_memcpy(&u[c * CH], &w, 16);
+            }
+            if constexpr (NRC > 0) {
+                if (solve) {
 #pragma unroll
-                for (int c = 0; c < NRC; ++c) {
-                    uint4 w = rowbuf[grp][NBC + c];
-                    __builtin_memcpy(&ub[c * CH], &w, 16);
+                    for (int c = 0; c < NRC; ++c) {
+                        uint4 w = rowbuf[grp][NBC + c];
+                        __builtin_memcpy(&ub[c * CH], &w, 16);
+                    }
                 }
             }
+        } else {
+            uint4 w = rowbuf[grp][j / CH];
+            __builtin_memcpy(&u[(j / CH) * CH], &w, 16);
         }
 
         const T piv = u[j];
@@ -237,13 +260,39 @@ register_lu_kernel(Problem p, int mode)
             if (pos[s] > j && !zero) {
                 const T l = lm[s];
                 a[s][j] = l;
+                if constexpr (!chunked) {
 #pragma unroll
-                for (int k = 0; k < NB; ++k)
-                    if (k > j) O::fms(a[s][k], l, u[k]);
-                if constexpr (NR > 0) {
-                    if (solve) {
+                    for (int k = 0; k < NB; ++k)
+                        if (k > j) O::fms(a[s][k], l, u[k]);
+                    if constexpr (NR > 0) {
+                        if (solve) {
 #pragma unroll
-                        for (int r2 = 0; r2 < NR; ++r2) O::fms(b[s][r2], l, ub[r2]);
+                            for (int r2 = 0; r2 < NR; ++r2) O::fms(b[s][r2], l, ub[r2]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < NBC; ++c) {
+                        if (c < j / CH) continue;
+                        T uc[CH];
+                        uint4 w = rowbuf[grp][c];
+                        __builtin_memcpy(uc, &w, 16);
+#pragma unroll
+                        for (int e = 0; e < CH; ++e)
+                            if (c * CH + e > j) O::fms(a[s][c * CH + e], l, uc[e]);
+                    }
+                    if constexpr (NR > 0) {
+                        if (solve) {
+#pragma unroll
+                            for (int c = 0; c < NRC; ++c) {
+                                T uc[CH];
+                                uint4 w = rowbuf[grp][NBC + c];
+                                __builtin_memcpy(uc, &w, 16);
+#pragma unroll
+                                for (int e = 0; e < CH; ++e)
+                                    if (c * CH + e < NR) O::fms(b[s][c * CH + e], l, uc[e]);
+                            }
+                        }
                     }
                 }
             }
