@@ -176,7 +176,7 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
             T piv = cv[0];
 #pragma unroll
             for (int v = 1; v < NW; ++v) {
-                const bool take = kv[v] > best || (kv[v] == best && pv[v] < ppos);
+                const bool take = (kv[v] > best) | ((kv[v] == best) & (pv[v] < ppos));   // no short circuit: no branch
                 best = take ? kv[v] : best;
                 ppos = take ? pv[v] : ppos;
                 vb = take ? v : vb;
@@ -203,22 +203,30 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
             const T r = O::recip(piv);
             const bool small = !(pm >= O::sfmin());
             // rows below the pivot take the update; the others keep their
-            // values (selected, not skipped, so that the whole step stays one
-            // block the scheduler can interleave with the next pivot search)
+            // values.  f32 selects (one select per element keeps the step a
+            // single block the scheduler can interleave with the next pivot
+            // search); f64 masks (a select costs two instructions there)
             const bool upd = pos > jj && pos < m && !zero;
             T l = O::mul(a[jj], r);
             if (__builtin_amdgcn_ballot_w64(small && upd) != 0) {
                 asm volatile("" ::: "memory");
                 if (small && upd) l = O::div(a[jj], piv);
             }
-            a[jj] = upd ? l : a[jj];
+            if constexpr (sizeof(T) == 4) {
+                a[jj] = upd ? l : a[jj];
 #pragma unroll
-            for (int c = 0; c < NB; ++c)
-                if (c > jj) {
-                    T t = a[c];
-                    O::fms(t, l, u[c]);
-                    a[c] = upd ? t : a[c];
-                }
+                for (int c = 0; c < NB; ++c)
+                    if (c > jj) {
+                        T t = a[c];
+                        O::fms(t, l, u[c]);
+                        a[c] = upd ? t : a[c];
+                    }
+            } else if (upd) {
+                a[jj] = l;
+#pragma unroll
+                for (int c = 0; c < NB; ++c)
+                    if (c > jj) O::fms(a[c], l, u[c]);
+            }
         }
         // rows to their final positions; L11 to LDS for the U12 solve
         if (tid < m) {
