@@ -29,9 +29,14 @@ FP32_ALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop x 2.4 GHz, no packe
 FP32_MFMA_PEAK_TFLOPS = 157.3
 FP64_PEAK_TFLOPS = 78.6
 METRIC = "batched gesv matrices/s + GFLOP/s (n=32 f32, n=256 f64), % of roofline"
+# sources of the kernel whose HBM counters a workload's summary records
+# (the summary is used only while these sources are unchanged)
+_C = "dense_linear_algebra_amd/csrc/"
 KERNEL_SOURCES = {
-    "register": ["dense_linear_algebra_amd/csrc/register_lu_kernel.h", "dense_linear_algebra_amd/csrc/register_lu_row16.h",
-                 "dense_linear_algebra_amd/csrc/device_ops.h"],
+    "sgesv_n16_b1024": [_C + "register_lu_row16.h", _C + "device_ops.h"],
+    "sgesv_n32_r8_b32768": [_C + "register_lu_row16.h", _C + "device_ops.h"],
+    "cgesv_n64_r16_b8192": [_C + "register_lu_kernel.h", _C + "device_ops.h"],
+    "dgesv_n256_b1024": [_C + "blocked_fused.hip", _C + "device_ops.h"],
 }
 
 
@@ -47,18 +52,21 @@ def algorithmic_flops(w) -> float:
     return f * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0)
 
 
-def source_hash(kind: str) -> str:
+def source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES.get(kind, []):
+    for rel in KERNEL_SOURCES.get(workload, []):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str, kind: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kind}_gesv_{workload}_counters.json")
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel
+    source; else None."""
+    if workload not in KERNEL_SOURCES:
+        return None
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -66,7 +74,7 @@ def traffic_from_profile(workload: str, kind: str):
             d = json.load(f)
     except Exception:
         return None
-    if d.get("source_hash") != source_hash(kind):
+    if d.get("source_hash") != source_hash(workload):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -89,13 +97,12 @@ def _counter_rows(db: str):
     return rows
 
 
-def write_counter_summary(workload: str, kind: str, kernel: str, fetch_db: str, write_db: str,
-                          copy_mb: int, commands):
+def write_counter_summary(workload: str, kernel: str, fetch_db: str, write_db: str, copy_mb: int, commands):
     """HBM bytes per launch of `kernel` from a FETCH_SIZE and a WRITE_SIZE run,
     each scaled by what the counter reads for the plain device copy of
     copy_mb MiB that the same run made first (bench.py --copy-probe-mb)."""
     w = lu_inputs.WORKLOADS[workload]
-    res = {"kernel": kernel, "workload": workload, "source_hash": source_hash(kind), "commands": list(commands)}
+    res = {"kernel": kernel, "workload": workload, "source_hash": source_hash(workload), "commands": list(commands)}
     per = {}
     for tag, db in (("fetch", fetch_db), ("write", write_db)):
         rows = _counter_rows(db)
@@ -116,7 +123,7 @@ def write_counter_summary(workload: str, kind: str, kernel: str, fetch_db: str, 
                        "write_size_kib": per["write"][1], "fetch_scale": fetch_scale, "write_scale": write_scale},
         "hbm_bytes_read_per_launch": rd, "hbm_bytes_written_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
         "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": (rd + wr) / alg})
-    path = os.path.join(ROOT, "profiles", f"{kind}_gesv_{workload}_counters.json")
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
     print(path)
@@ -156,7 +163,7 @@ def main():
         kern, fdb, wdb = args.counters_summary
         mb = args.copy_probe_mb or 256
         base = f"python3 bench.py --workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mb {mb}"
-        write_counter_summary(args.workload, "register", kern, fdb, wdb, mb,
+        write_counter_summary(args.workload, kern, fdb, wdb, mb,
                               [f"rocprofv3 --pmc FETCH_SIZE -d <dir> -o f -- {base}",
                                f"rocprofv3 --pmc WRITE_SIZE -d <dir> -o w -- {base}"])
         return
@@ -245,7 +252,7 @@ def main():
     kind = "register" if tier in (lib.TIER_TINY, lib.TIER_CTA) else "blocked"
     if kind == "register":
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profile(w.name, kind),
+                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profile(w.name),
                 "kernel_ms": kernel_ms, "algorithmic_bytes_per_launch": bytes_launch}
     else:
         # blocked tier: the factorisation is the dominant part of the step;
@@ -271,7 +278,8 @@ def main():
         fused = lib.batchlu_select_tier(t, 0, w.n, 0, w.batch) == lib.TIER_BLOCKED and w.n <= 256 and \
             np.dtype(w.dtype).kind == "f"
         roof = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
-                "traffic": None, "kernel_ms": gms, "algorithmic_flops_per_launch": getrf_flops,
+                "traffic": traffic_from_profile(w.name) if fused else None,
+                "kernel_ms": gms, "algorithmic_flops_per_launch": getrf_flops,
                 "scope": ("batchlu_getrf = one lu_fused_kernel launch" if fused else
                           "batchlu_getrf = its panel, U12-solve, update and interchange launches"),
                 "whole_step": {"ms": kernel_ms, "tflops": flops_launch / (kernel_ms * 1e-3) / 1e12}}
