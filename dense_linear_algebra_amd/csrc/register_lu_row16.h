@@ -1,22 +1,27 @@
 // register_lu_row16.h -- register-resident LU and fused gesv for float
 // matrices of order 9..32, one matrix per 16-lane DPP row.
 //
-// Same method and operation order as register_lu_kernel.h (lazy relabel,
-// DPP argmax with lowest-position ties, one fma per element and step), with
-// the pivot row moved by DPP instead of LDS broadcast reads:
-//   - the owner lane writes the pivot row to a per-matrix LDS row; each of
-//     the 16 lanes of the matrix reads back ONE 16-byte chunk of it (one
-//     ds_read_b128 per step instead of one per chunk);
-//   - every element of the pivot row then reaches the whole matrix by a
-//     row_newbcast DPP move from the lane holding its chunk (the source lane
-//     is a compile-time constant because the row chunk index is);
-//   - after elimination the rows are put in position order once (through a
-//     one-chunk LDS stage), so the back substitution broadcasts x_k from a
-//     static lane by DPP as well and needs no LDS round trip per step, and
-//     L, U and X are stored with row-contiguous vector writes.
+// Same method and per-element operation order as register_lu_kernel.h
+// (lazy relabel of row positions, argmax with lowest-position ties, one fma
+// per element and step), arranged so that the rank-1 update runs with every
+// lane enabled:
+//   - the pivot row of step j is published into a per-matrix LDS record
+//     (row j: the 16-byte chunks from the one holding column j onwards, then
+//     the right-hand-side chunks); each of the 16 lanes reads back one chunk;
+//   - the update a_ik -= l_i u_jk takes u_jk straight from the lane holding
+//     its chunk through a row_newbcast DPP operand of v_fmac_f32, so no
+//     broadcast copy of the pivot row is made;
+//   - rows already chosen as pivots are updated too (their multipliers are
+//     meaningless, which saves the per-row exec masks): their U and
+//     right-hand-side parts are taken from the record at the end, their L
+//     parts are never written after they become pivots;
+//   - the back substitution reads U and y from the record, one lane per
+//     (matrix, right-hand-side column), with the oracle's descending order of
+//     subtractions per entry; X leaves as contiguous columns.
 // The pages' tiny tier publishes the pivot row through local memory (LU
-// page, local-row broadcast paragraph); here the broadcast itself rides on
-// DPP, which a 16-lane row of a wave64 supports natively.
+// page, local-row broadcast paragraph); here the broadcast rides on DPP,
+// which a 16-lane row of a wave64 supports natively, and the local copy
+// doubles as the record of U.
 #pragma once
 
 #include <type_traits>
@@ -38,12 +43,145 @@ __device__ inline float bcast(float v) {
                                                               false));
 }
 
+// d_t -= u_t(lane L) * l for the four elements of one chunk, for one or two
+// rows (l0, l1).  v_fmac_f32 with a DPP source: d = (-u[lane L]) * l + d, the
+// same rounding as fma(-l, u, d).  The leading s_nop gives the two wait
+// states a DPP source needs after a VALU write (the compiler's hazard
+// tracking does not look inside asm).
+template <int L>
+__device__ inline void fnma_chunk(float (&d0)[4], const float (&u)[4], float l0) {
+    static_assert(L >= 0 && L < 16, "lane");
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, -%4, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, -%5, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, -%6, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, -%7, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf"
+        : "+v"(d0[0]), "+v"(d0[1]), "+v"(d0[2]), "+v"(d0[3])
+        : "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(l0), "n"(L));
+}
+template <int L>
+__device__ inline void fnma_chunk(float (&d0)[4], float (&d1)[4], const float (&u)[4], float l0, float l1) {
+    static_assert(L >= 0 && L < 16, "lane");
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, -%8, %12 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, -%9, %12 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, -%10, %12 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, -%11, %12 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, -%8, %13 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, -%9, %13 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, -%10, %13 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, -%11, %13 row_newbcast:%14 row_mask:0xf bank_mask:0xf"
+        : "+v"(d0[0]), "+v"(d0[1]), "+v"(d0[2]), "+v"(d0[3]), "+v"(d1[0]), "+v"(d1[1]), "+v"(d1[2]), "+v"(d1[3])
+        : "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(l0), "v"(l1), "n"(L));
+}
+
+// The same for elements E..3 of a chunk (the rest of the chunk holding the
+// pivot column).
+template <int L, int E>
+__device__ inline void fnma_tail(float (&d0)[4], const float (&u)[4], float l0) {
+    static_assert(L >= 0 && L < 16 && E >= 1 && E <= 3, "lane / element");
+    if constexpr (E == 1) {
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, -%3, %6 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %1, -%4, %6 row_newbcast:%7 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %2, -%5, %6 row_newbcast:%7 row_mask:0xf bank_mask:0xf"
+            : "+v"(d0[1]), "+v"(d0[2]), "+v"(d0[3])
+            : "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(l0), "n"(L));
+    } else if constexpr (E == 2) {
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, -%2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %1, -%3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+            : "+v"(d0[2]), "+v"(d0[3])
+            : "v"(u[2]), "v"(u[3]), "v"(l0), "n"(L));
+    } else {
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+            : "+v"(d0[3])
+            : "v"(u[3]), "v"(l0), "n"(L));
+    }
+}
+template <int L, int E>
+__device__ inline void fnma_tail(float (&d0)[4], float (&d1)[4], const float (&u)[4], float l0, float l1) {
+    static_assert(L >= 0 && L < 16 && E >= 1 && E <= 3, "lane / element");
+    if constexpr (E == 1) {
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, -%6, %9 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %1, -%7, %9 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %2, -%8, %9 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %3, -%6, %10 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %4, -%7, %10 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %5, -%8, %10 row_newbcast:%11 row_mask:0xf bank_mask:0xf"
+            : "+v"(d0[1]), "+v"(d0[2]), "+v"(d0[3]), "+v"(d1[1]), "+v"(d1[2]), "+v"(d1[3])
+            : "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(l0), "v"(l1), "n"(L));
+    } else if constexpr (E == 2) {
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, -%4, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %1, -%5, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %2, -%4, %7 row_newbcast:%8 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %3, -%5, %7 row_newbcast:%8 row_mask:0xf bank_mask:0xf"
+            : "+v"(d0[2]), "+v"(d0[3]), "+v"(d1[2]), "+v"(d1[3])
+            : "v"(u[2]), "v"(u[3]), "v"(l0), "v"(l1), "n"(L));
+    } else {
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, -%2, %3 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_dpp %1, -%2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+            : "+v"(d0[3]), "+v"(d1[3])
+            : "v"(u[3]), "v"(l0), "v"(l1), "n"(L));
+    }
+}
+
 template <int I, int N, typename F>
 __device__ inline void static_for(F&& f) {
     if constexpr (I < N) {
         f(std::integral_constant<int, I>{});
         static_for<I + 1, N>(f);
     }
+}
+
+// Record layout per matrix: row j holds chunks j/4 .. NBC-1 of its A part,
+// then its NRC right-hand-side chunks.  rec_off(j) = first chunk of row j.
+template <int NBC, int NRC>
+__host__ __device__ constexpr int rec_off(int j) {
+    int o = 0;
+    for (int i = 0; i < j; ++i) o += NBC - i / 4 + NRC;
+    return o;
+}
+template <int NBC, int NRC>
+__device__ inline int rec_off_dyn(int j) {
+    const int q = j >> 2, t = j & 3;
+    return 4 * (q * (NBC + NRC) - (q * (q - 1)) / 2) + t * (NBC + NRC - q);
+}
+
+// 1/x rounded once: v_rcp_f32 and one Newton step agree with the IEEE
+// quotient for every |x| in [2^-125, 2^125] (checked exhaustively on the
+// device); outside that range the full division is taken.
+__device__ inline float recip_fast(float x) {
+    const float r0 = __builtin_amdgcn_rcpf(x);
+    const float e = __builtin_fmaf(-x, r0, 1.0f);
+    return __builtin_fmaf(e, r0, r0);
+}
+__device__ inline bool recip_fast_ok(float ax) { return ax >= 0x1p-125f && ax <= 0x1p125f; }
+// the reciprocal of a pivot, the same bits wherever it is formed
+__device__ inline float recip_step(float piv) {
+    float r = recip_fast(piv);
+    const bool ok = recip_fast_ok(__builtin_fabsf(piv));
+    if (__builtin_amdgcn_ballot_w64(!ok) != 0) {
+        asm volatile("" ::: "memory");
+        if (!ok) r = 1.0f / piv;
+    }
+    return r;
+}
+
+// two floats into LDS at byte address addr + 4*O0 and addr + 4*O1.  The
+// pivot row is published this way: ds_write2_b32 takes any two registers,
+// where a 16-byte store would need the row's chunks in aligned register
+// quads (a copy per element otherwise).  The clobber keeps later LDS reads
+// after it.
+template <int O0, int O1>
+__device__ inline void ds_write2(uint32_t addr, float x0, float x1) {
+    static_assert(O0 >= 0 && O0 < 256 && O1 >= 0 && O1 < 256, "ds_write2_b32 offsets are 8-bit dword counts");
+    asm volatile("ds_write2_b32 %0, %1, %2 offset0:%3 offset1:%4" ::"v"(addr), "v"(x0), "v"(x1), "n"(O0), "n"(O1)
+                 : "memory");
 }
 
 template <int NB, int NR>
@@ -56,13 +194,18 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
     constexpr int NRC = (NR + 3) / 4;            // chunks of a B row
     constexpr int NRP = NRC * 4 > 0 ? NRC * 4 : 1;
     constexpr int ROWC = NBC + NRC;              // chunks of a row: at most 16
+    constexpr int RECC = rec_off<NBC, NRC>(NB);  // record chunks per matrix
     static_assert(NB == 16 || NB == 32, "row16 handles buckets 16 and 32");
     static_assert(ROWC <= 16, "a row must fit one chunk per lane");
 
-    __shared__ uint4 rowbuf[GPB][ROWC];          // the pivot row of the step
-    __shared__ uint4 stage[GPB][NB];             // one chunk column, rows by position
-    __shared__ float diag[GPB][NB];              // 1/u_jj
-    __shared__ float dval[GPB][NB];              // u_jj
+    // published pivot rows, by position.  The four matrices of a wavefront
+    // sit two chunks apart beyond their records (a record is a multiple of
+    // 64 dwords), so that their owners' stores fall on different LDS banks;
+    // the padding stays inside the wavefront's share so that three blocks
+    // still fit one compute unit.
+    constexpr int RSTRIDE = RECC + 2;
+    __shared__ uint4 rec[kWaves][3 * RSTRIDE + RECC];
+    __shared__ int ppos[GPB];                    // position the pivot row came from
 
     const int lane = threadIdx.x & 63;
     const int grp = (threadIdx.x >> 6) * 4 + (lane >> 4);
@@ -81,26 +224,24 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
     int pos[RPL];
 
     // ---- load ---------------------------------------------------------------
-    const bool full = (n == NB) && ((p.lda & (RPL - 1)) == 0) && (((uintptr_t)A) % (4 * RPL) == 0);
 #pragma unroll
-    for (int s = 0; s < RPL; ++s) pos[s] = li * RPL + s;
-    if (full) {
+    for (int s = 0; s < RPL; ++s) pos[s] = li + 16 * s;
+    if (n == NB && p.lda == NB) {
 #pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            if constexpr (RPL == 2) {
-                const float2 w = *(const float2*)(A + li * 2 + (long long)k * p.lda);
-                a[0][k] = w.x;
-                a[1][k] = w.y;
-            } else {
-                a[0][k] = A[li + (long long)k * p.lda];
-            }
-        }
+        for (int k = 0; k < NB; ++k)
+#pragma unroll
+            for (int s = 0; s < RPL; ++s) a[s][k] = A[li + 16 * s + k * NB];
+    } else if (n == NB) {
+#pragma unroll
+        for (int k = 0; k < NB; ++k)
+#pragma unroll
+            for (int s = 0; s < RPL; ++s) a[s][k] = A[li + 16 * s + (long long)k * p.lda];
     } else {
 #pragma unroll
         for (int k = 0; k < NB; ++k)
 #pragma unroll
             for (int s = 0; s < RPL; ++s) {
-                const int row = li * RPL + s;
+                const int row = li + 16 * s;
                 float v = (row == k) ? 1.0f : 0.0f;
                 if (k < n && row < n) v = A[row + (long long)k * p.lda];
                 a[s][k] = v;
@@ -110,7 +251,7 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
     for (int r = 0; r < NRP; ++r)
 #pragma unroll
         for (int s = 0; s < RPL; ++s) {
-            const int row = li * RPL + s;
+            const int row = li + 16 * s;
             float v = 0.0f;
             if (solve && r < NR && r < p.nrhs && row < n) v = B[row + (long long)r * p.ldb];
             b[s][r] = v;
@@ -120,11 +261,21 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
     int pivrec[NB / 16];
 #pragma unroll
     for (int t = 0; t < NB / 16; ++t) pivrec[t] = 0;
+    float rd[NB];                 // 1/u_jj, identical in the 16 lanes of a matrix
+    uint32_t smallmask = 0;       // steps whose pivot is below the smallest normal
+    uint4* const rbase = &rec[grp >> 2][(grp & 3) * RSTRIDE];
+    int* const ppos_g = &ppos[grp];
+    const uint32_t lds_rec = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)rbase;
+    // lane li reads chunk li of each published row (lanes past the row read
+    // its first chunk); rec_off(j) - j/4 >= 0 keeps every address in range
+    const uint4* const rread = rbase + (li < ROWC ? li : 0);
 
     // ---- elimination ----------------------------------------------------------
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        if (j >= n) continue;
+    static_for<0, NB>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int J4 = j / 4;
+        constexpr int RO = rec_off<NBC, NRC>(j) - J4;   // record row j, as chunk J4 + c at RO + c
+        if (j >= n) return;
         uint32_t key[RPL];
         uint32_t kmax = 0;
 #pragma unroll
@@ -134,200 +285,235 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
             kmax = kk > kmax ? kk : kmax;
         }
         kmax = group_max<16>(kmax);
-        int q = 0x7fffffff;
+        bool hit[RPL];
 #pragma unroll
-        for (int s = 0; s < RPL; ++s)
-            if (key[s] == kmax && pos[s] < q) q = pos[s];
-        const int piv_pos = group_min<16>(q);
-        if (li == j % 16) pivrec[j / 16] = piv_pos;
-
-        // the owner writes its row from the chunk holding column j
+        for (int s = 0; s < RPL; ++s) hit[s] = key[s] == kmax;
+        // one maximal row per matrix (the usual case) needs no position
+        // reduction; otherwise the lowest position among the maximal wins
+        uint64_t hits = 0, both = ~0ull;
 #pragma unroll
         for (int s = 0; s < RPL; ++s) {
-            if (pos[s] == piv_pos) {
-#pragma unroll
-                for (int c = 0; c < NBC; ++c) {
-                    if (c < j / 4) continue;
-                    rowbuf[grp][c] = make_uint4(__float_as_uint(a[s][4 * c]), __float_as_uint(a[s][4 * c + 1]),
-                                                __float_as_uint(a[s][4 * c + 2]), __float_as_uint(a[s][4 * c + 3]));
-                }
-                if constexpr (NRC > 0) {
-                    if (solve) {
-#pragma unroll
-                        for (int c = 0; c < NRC; ++c)
-                            rowbuf[grp][NBC + c] =
-                                make_uint4(__float_as_uint(b[s][4 * c]), __float_as_uint(b[s][4 * c + 1]),
-                                           __float_as_uint(b[s][4 * c + 2]), __float_as_uint(b[s][4 * c + 3]));
-                    }
-                }
-            }
+            const uint64_t bs = __builtin_amdgcn_ballot_w64(hit[s]);
+            hits |= bs;
+            both &= bs;
         }
-#pragma unroll
-        for (int s = 0; s < RPL; ++s)
-            pos[s] = (pos[s] == piv_pos) ? j : (pos[s] == j ? piv_pos : pos[s]);
-
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // lane li holds chunk li of the pivot row
-        const uint4 chw = rowbuf[grp][li < ROWC ? li : 0];
-        const float ch[4] = {__uint_as_float(chw.x), __uint_as_float(chw.y), __uint_as_float(chw.z),
-                             __uint_as_float(chw.w)};
-        float u[NB];
-        float ub[NRP];
-        static_for<0, NB>([&](auto kc) {
-            constexpr int k = decltype(kc)::value;
-            if (k >= j) u[k] = bcast<k / 4>(ch[k % 4]);
-        });
-        if constexpr (NR > 0) {
-            if (solve)
-                static_for<0, NR>([&](auto rc) {
-                    constexpr int r2 = decltype(rc)::value;
-                    ub[r2] = bcast<NBC + r2 / 4>(ch[r2 % 4]);
-                });
-        }
-
-        const float piv = u[j];
-        const float pm = __builtin_fabsf(piv);
-        const bool zero = pm == 0.0f;
-        if (zero && info == 0) info = j + 1;
-        const float r = 1.0f / piv;
-        const bool small = !(pm >= O::sfmin());
-        if (li == 0) {
-            diag[grp][j] = r;
-            dval[grp][j] = piv;
-        }
-        float lm[RPL];
-#pragma unroll
-        for (int s = 0; s < RPL; ++s) lm[s] = a[s][j] * r;
-        if (__builtin_amdgcn_ballot_w64(small) != 0) {
-            asm volatile("" ::: "memory");
+        const bool unique = __builtin_popcountll(hits) == 4 && (RPL == 1 || both == 0);
+        int pp = -1;
+        if (!unique) {
+            int q = 0x7fffffff;
 #pragma unroll
             for (int s = 0; s < RPL; ++s)
-                if (small) lm[s] = a[s][j] / piv;
+                if (hit[s] && pos[s] < q) q = pos[s];
+            pp = group_min<16>(q);
         }
+        bool own[RPL];
+#pragma unroll
+        for (int s = 0; s < RPL; ++s) own[s] = unique ? hit[s] : pos[s] == pp;
+
+        // the owner publishes its row (A chunks from the one holding column
+        // j, then B) and where it came from
 #pragma unroll
         for (int s = 0; s < RPL; ++s) {
-            if (pos[s] > j && !zero) {
-                const float l = lm[s];
-                a[s][j] = l;
+            if (own[s]) {
+                const uint32_t ra = lds_rec + 16u * (RO + J4);   // start of record row j
+                static_for<0, NB / 2 - 2 * J4>([&](auto kc) {
+                    constexpr int e = 2 * decltype(kc)::value;
+                    ds_write2<e, e + 1>(ra, a[s][4 * J4 + e], a[s][4 * J4 + e + 1]);
+                });
+                if constexpr (NRC > 0) {
+                    static_for<0, 2 * NRC>([&](auto rc) {
+                        constexpr int e = 2 * decltype(rc)::value;
+                        ds_write2<NB - 4 * J4 + e, NB - 4 * J4 + e + 1>(ra, b[s][e], b[s][e + 1]);
+                    });
+                }
+                *ppos_g = pos[s];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        const uint4 chw = rread[RO];
+        const int piv_pos = *ppos_g;
+        const float ch[4] = {__uint_as_float(chw.x), __uint_as_float(chw.y), __uint_as_float(chw.z),
+                             __uint_as_float(chw.w)};
+        if (li == j % 16) pivrec[j / 16] = piv_pos;
 #pragma unroll
-                for (int k = 0; k < NB; ++k)
-                    if (k > j) a[s][k] = __builtin_fmaf(-l, u[k], a[s][k]);
-                if constexpr (NR > 0) {
-                    if (solve)
+        for (int s = 0; s < RPL; ++s) pos[s] = own[s] ? j : (pos[s] == j ? piv_pos : pos[s]);
+
+        const float piv = bcast<J4>(ch[j % 4]);
+        const float pm = __builtin_fabsf(piv);
+        const bool zero = pm == 0.0f;
+        if (zero && info == 0 && j < n) info = j + 1;
+        float r = recip_step(piv);
+        rd[j] = r;
+        const bool small = !(pm >= O::sfmin());
+        if (small) smallmask |= 1u << j;
+        // every row of the matrix is updated (rows already chosen get values
+        // that are never used); a zero pivot skips the step for its matrix
+        if (!zero) {
+            // multipliers l = a * r; a / pivot where the pivot is below the
+            // smallest normal
+            float q[RPL];
+            const bool anysmall = __builtin_amdgcn_ballot_w64(small) != 0;
+            if (anysmall) {
 #pragma unroll
-                        for (int r2 = 0; r2 < NR; ++r2) b[s][r2] = __builtin_fmaf(-l, ub[r2], b[s][r2]);
+                for (int s = 0; s < RPL; ++s) q[s] = a[s][j] / piv;
+            }
+#pragma unroll
+            for (int s = 0; s < RPL; ++s) a[s][j] = a[s][j] * r;
+            if (anysmall) {
+#pragma unroll
+                for (int s = 0; s < RPL; ++s)
+                    if (small) a[s][j] = q[s];
+            }
+            float lm[RPL];
+#pragma unroll
+            for (int s = 0; s < RPL; ++s) lm[s] = a[s][j];
+            // rest of the chunk holding column j
+            if constexpr (j % 4 != 3) {
+                if constexpr (RPL == 2) {
+                    fnma_tail<J4, j % 4 + 1>(*reinterpret_cast<float(*)[4]>(&a[0][4 * J4]), *reinterpret_cast<float(*)[4]>(&a[1][4 * J4]), ch, lm[0], lm[1]);
+                } else {
+                    fnma_tail<J4, j % 4 + 1>(*reinterpret_cast<float(*)[4]>(&a[0][4 * J4]), ch, lm[0]);
                 }
             }
-        }
-    }
-
-    // ---- rows into position order (one chunk column at a time) -------------
-    // slot s of lane li then holds the row at position li*RPL + s
-#pragma unroll
-    for (int c = 0; c < ROWC; ++c) {
-        if (c >= NBC && !solve) continue;
-#pragma unroll
-        for (int s = 0; s < RPL; ++s) {
-            float* src = c < NBC ? &a[s][4 * c] : &b[s][4 * (c - NBC)];
-            stage[grp][pos[s]] = make_uint4(__float_as_uint(src[0]), __float_as_uint(src[1]),
-                                            __float_as_uint(src[2]), __float_as_uint(src[3]));
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int s = 0; s < RPL; ++s) {
-            const uint4 w = stage[grp][li * RPL + s];
-            float* dst = c < NBC ? &a[s][4 * c] : &b[s][4 * (c - NBC)];
-            dst[0] = __uint_as_float(w.x);
-            dst[1] = __uint_as_float(w.y);
-            dst[2] = __uint_as_float(w.z);
-            dst[3] = __uint_as_float(w.w);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-
-    // ---- back substitution, x_k broadcast by DPP from its static lane -------
-    if constexpr (NR > 0) {
-        if (solve) {
-            float rd[RPL], dv[RPL];
-#pragma unroll
-            for (int s = 0; s < RPL; ++s) {
-                rd[s] = diag[grp][li * RPL + s];
-                dv[s] = dval[grp][li * RPL + s];
-            }
-            static_for<0, NB>([&](auto ic) {
-                constexpr int k = NB - 1 - decltype(ic)::value;
-                constexpr int ks = k % RPL;
-                constexpr int kl = k / RPL;
-                if (k < n) {
-                    // the owner (lane kl, slot ks) forms x_k; every lane reads it by DPP
-                    float own[NR];
-#pragma unroll
-                    for (int r2 = 0; r2 < NR; ++r2) own[r2] = b[ks][r2] * rd[ks];
-                    const bool tiny = !(__builtin_fabsf(dv[ks]) >= O::sfmin());
-                    if (__builtin_amdgcn_ballot_w64(tiny && li == kl) != 0) {
-                        asm volatile("" ::: "memory");
-                        if (tiny)
-#pragma unroll
-                            for (int r2 = 0; r2 < NR; ++r2) own[r2] = b[ks][r2] / dv[ks];
+            // whole chunks after it, then the right-hand sides
+            static_for<J4 + 1, ROWC>([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                if constexpr (c < NBC) {
+                    if constexpr (RPL == 2) {
+                        fnma_chunk<c>(*reinterpret_cast<float(*)[4]>(&a[0][4 * c]), *reinterpret_cast<float(*)[4]>(&a[1][4 * c]), ch, lm[0], lm[1]);
+                    } else {
+                        fnma_chunk<c>(*reinterpret_cast<float(*)[4]>(&a[0][4 * c]), ch, lm[0]);
                     }
-                    float xk[NR];
+                } else {
+                    constexpr int cb = c - NBC;
+                    if constexpr (4 * cb + 4 <= NR) {
+                        if constexpr (RPL == 2) {
+                            fnma_chunk<c>(*reinterpret_cast<float(*)[4]>(&b[0][4 * cb]), *reinterpret_cast<float(*)[4]>(&b[1][4 * cb]), ch, lm[0], lm[1]);
+                        } else {
+                            fnma_chunk<c>(*reinterpret_cast<float(*)[4]>(&b[0][4 * cb]), ch, lm[0]);
+                        }
+                    } else {
 #pragma unroll
-                    for (int r2 = 0; r2 < NR; ++r2) xk[r2] = bcast<kl>(own[r2]);
-                    if (li == kl) {
+                        for (int t = 0; t < 4; ++t) {
+                            if (4 * cb + t >= NR) continue;
+                            const float u = bcast<c>(ch[t]);
 #pragma unroll
-                        for (int r2 = 0; r2 < NR; ++r2) b[ks][r2] = xk[r2];
-                    }
-#pragma unroll
-                    for (int s = 0; s < RPL; ++s) {
-                        if (li * RPL + s < k) {
-#pragma unroll
-                            for (int r2 = 0; r2 < NR; ++r2) b[s][r2] = __builtin_fmaf(-a[s][k], xk[r2], b[s][r2]);
+                            for (int s = 0; s < RPL; ++s) b[s][4 * cb + t] = __builtin_fmaf(-lm[s], u, b[s][4 * cb + t]);
                         }
                     }
                 }
             });
         }
+    });
+
+    // ---- L, U and ipiv out ------------------------------------------------------
+    // Each row leaves from the lane that held it, to its final position: the
+    // L part from registers, the rest (U, from the chunk holding the diagonal
+    // on) from the record.  Within one column the 16 lanes of a matrix write
+    // one 128-byte line.
+    if (live) {
+        const bool contig = n == NB && p.lda == NB;
+#pragma unroll
+        for (int s = 0; s < RPL; ++s) {
+            const int pr = pos[s];
+            const int q = pr >> 2;
+            // chunk c of row pr at rrow[c] for c >= q (in range for every pr)
+            const uint4* const rrow = rbase + (rec_off_dyn<NBC, NRC>(pr) - q);
+            float v[NB];
+#pragma unroll
+            for (int c = 0; c < NBC; ++c) {
+                const uint4 w = rrow[c];
+                // read every chunk, then select: no per-lane branches
+                asm volatile("" ::"v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w));
+                const bool fromrec = c >= q;
+                v[4 * c] = fromrec ? __uint_as_float(w.x) : a[s][4 * c];
+                v[4 * c + 1] = fromrec ? __uint_as_float(w.y) : a[s][4 * c + 1];
+                v[4 * c + 2] = fromrec ? __uint_as_float(w.z) : a[s][4 * c + 2];
+                v[4 * c + 3] = fromrec ? __uint_as_float(w.w) : a[s][4 * c + 3];
+            }
+            float* const Ar = A + pr;
+            if (contig) {
+#pragma unroll
+                for (int k = 0; k < NB; ++k) Ar[k * NB] = v[k];
+            } else if (pr < n) {
+#pragma unroll
+                for (int k = 0; k < NB; ++k)
+                    if (k < n) Ar[(long long)k * p.lda] = v[k];
+            }
+        }
+        int* ipiv = p.ipiv + m * p.sP;
+#pragma unroll
+        for (int t = 0; t < NB / 16; ++t) {
+            const int j = t * 16 + li;
+            if (j < n) ipiv[j] = pivrec[t] + 1;
+        }
+        if (li == 0) p.info[m] = info;
     }
 
-    // ---- store (rows now in position order) ----------------------------------
-    if (!live) return;
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-        if (k >= n) continue;
-        if (full && RPL == 2) {
-            *(float2*)(A + li * 2 + (long long)k * p.lda) = make_float2(a[0][k], a[RPL - 1][k]);
-        } else {
-#pragma unroll
-            for (int s = 0; s < RPL; ++s)
-                if (li * RPL + s < n) A[li * RPL + s + (long long)k * p.lda] = a[s][k];
-        }
-    }
-    int* ipiv = p.ipiv + m * p.sP;
-#pragma unroll
-    for (int t = 0; t < NB / 16; ++t) {
-        const int j = t * 16 + li;
-        if (j < n) ipiv[j] = pivrec[t] + 1;
-    }
-    if (li == 0) p.info[m] = info;
+    // ---- back substitution from the record: lane li solves column li ---------
     if constexpr (NR > 0) {
-        if (solve && info == 0) {
-            const bool bfull = full && ((p.ldb & (RPL - 1)) == 0) && (((uintptr_t)B) % (4 * RPL) == 0);
+        if (solve) {
+            const int rc = li < NR ? li : NR - 1;
+            const float* const yb = reinterpret_cast<const float*>(rbase) + rc;
+            float x[NB];
+            const bool fast = n == NB && __builtin_amdgcn_ballot_w64(smallmask != 0) == 0;
+            if (fast) {
+                static_for<0, NB>([&](auto ic) {
+                    constexpr int k = NB - 1 - decltype(ic)::value;
+                    constexpr int RO = rec_off<NBC, NRC>(k) - k / 4;
+                    float acc = yb[4 * (RO + NBC)];
 #pragma unroll
-            for (int r2 = 0; r2 < NR; ++r2) {
-                if (r2 >= p.nrhs) continue;
-                if (bfull && RPL == 2) {
-                    *(float2*)(B + li * 2 + (long long)r2 * p.ldb) = make_float2(b[0][r2], b[RPL - 1][r2]);
+                    for (int c = NBC - 1; c >= k / 4; --c) {
+                        const uint4 w = rbase[RO + c];
+                        const float u[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                                            __uint_as_float(w.w)};
+#pragma unroll
+                        for (int t = 3; t >= 0; --t)
+                            if (4 * c + t > k) acc = __builtin_fmaf(-u[t], x[4 * c + t], acc);
+                    }
+                    x[k] = acc * rd[k];
+                });
+            } else {
+                static_for<0, NB>([&](auto ic) {
+                    constexpr int k = NB - 1 - decltype(ic)::value;
+                    constexpr int RO = rec_off<NBC, NRC>(k) - k / 4;
+                    if (k < n) {
+                        float acc = yb[4 * (RO + NBC)];
+#pragma unroll
+                        for (int c = NBC - 1; c >= k / 4; --c) {
+                            const uint4 w = rbase[RO + c];
+                            const float u[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                                                __uint_as_float(w.w)};
+#pragma unroll
+                            for (int t = 3; t >= 0; --t)
+                                if (4 * c + t > k && 4 * c + t < n) acc = __builtin_fmaf(-u[t], x[4 * c + t], acc);
+                        }
+                        const uint4 w = rbase[RO + k / 4];
+                        const float u[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
+                                            __uint_as_float(w.w)};
+                        if ((smallmask >> k) & 1u)
+                            x[k] = acc / u[k % 4];
+                        else
+                            x[k] = acc * rd[k];
+                    } else {
+                        x[k] = 0.0f;
+                    }
+                });
+            }
+            if (live && info == 0 && li < NR && li < p.nrhs) {
+                float* const Xc = B + (long long)li * p.ldb;
+                if (n == NB && (((uintptr_t)Xc) % 16) == 0) {
+#pragma unroll
+                    for (int c = 0; c < NBC; ++c)
+                        *reinterpret_cast<float4*>(Xc + 4 * c) = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2],
+                                                                             x[4 * c + 3]);
                 } else {
 #pragma unroll
-                    for (int s = 0; s < RPL; ++s)
-                        if (li * RPL + s < n) B[li * RPL + s + (long long)r2 * p.ldb] = b[s][r2];
+                    for (int k = 0; k < NB; ++k)
+                        if (k < n) Xc[k] = x[k];
                 }
             }
         }
