@@ -130,6 +130,20 @@ __device__ inline void fnma_tail(float (&d0)[4], float (&d1)[4], const float (&u
     }
 }
 
+// maximum of a signed value over each 16-lane row (DPP; every source lane
+// of these patterns lies inside the row)
+__device__ inline int group_max16_i32(int v) {
+    int o = (int)exchange32<1>((uint32_t)v, 0x80000000u);
+    v = o > v ? o : v;
+    o = (int)exchange32<2>((uint32_t)v, 0x80000000u);
+    v = o > v ? o : v;
+    o = (int)exchange32<4>((uint32_t)v, 0x80000000u);
+    v = o > v ? o : v;
+    o = (int)exchange32<8>((uint32_t)v, 0x80000000u);
+    v = o > v ? o : v;
+    return v;
+}
+
 template <int I, int N, typename F>
 __device__ inline void static_for(F&& f) {
     if constexpr (I < N) {
@@ -257,12 +271,12 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
             b[s][r] = v;
         }
 
-    int info = 0;
     int pivrec[NB / 16];
 #pragma unroll
     for (int t = 0; t < NB / 16; ++t) pivrec[t] = 0;
     float rd[NB];                 // 1/u_jj, identical in the 16 lanes of a matrix
-    uint32_t smallmask = 0;       // steps whose pivot is below the smallest normal
+    bool wave_zero = false;       // some matrix of the wavefront met a zero pivot
+    bool wave_small = false;      // some pivot below the smallest normal
     uint4* const rbase = &rec[grp >> 2][(grp & 3) * RSTRIDE];
     int* const ppos_g = &ppos[grp];
     const uint32_t lds_rec = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)rbase;
@@ -276,39 +290,42 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
         constexpr int J4 = j / 4;
         constexpr int RO = rec_off<NBC, NRC>(j) - J4;   // record row j, as chunk J4 + c at RO + c
         if (j >= n) return;
-        uint32_t key[RPL];
-        uint32_t kmax = 0;
+        // candidate keys: the bits of |a| with every NaN clamped just above
+        // +inf (so NaNs tie and rank first), -1 for rows already chosen
+        int key[RPL];
+        int kmax = -1;
 #pragma unroll
         for (int s = 0; s < RPL; ++s) {
-            const uint32_t kk = (pos[s] >= j) ? pivot_key(__builtin_fabsf(a[s][j])) : 0u;
+            const uint32_t bits = __float_as_uint(a[s][j]) & 0x7fffffffu;
+            const int kk = (pos[s] >= j) ? (int)(bits < 0x7f800001u ? bits : 0x7f800001u) : -1;
             key[s] = kk;
             kmax = kk > kmax ? kk : kmax;
         }
-        kmax = group_max<16>(kmax);
-        bool hit[RPL];
-#pragma unroll
-        for (int s = 0; s < RPL; ++s) hit[s] = key[s] == kmax;
+        kmax = group_max16_i32(kmax);
         // one maximal row per matrix (the usual case) needs no position
-        // reduction; otherwise the lowest position among the maximal wins
+        // reduction; otherwise the lowest position among the maximal wins.
+        // Ownership stays in scalar lane masks.
+        uint64_t om[RPL];
         uint64_t hits = 0, both = ~0ull;
 #pragma unroll
         for (int s = 0; s < RPL; ++s) {
-            const uint64_t bs = __builtin_amdgcn_ballot_w64(hit[s]);
-            hits |= bs;
-            both &= bs;
+            om[s] = __builtin_amdgcn_ballot_w64(key[s] == kmax);
+            hits |= om[s];
+            both &= om[s];
         }
         const bool unique = __builtin_popcountll(hits) == 4 && (RPL == 1 || both == 0);
-        int pp = -1;
         if (!unique) {
             int q = 0x7fffffff;
 #pragma unroll
             for (int s = 0; s < RPL; ++s)
-                if (hit[s] && pos[s] < q) q = pos[s];
-            pp = group_min<16>(q);
+                if (key[s] == kmax && pos[s] < q) q = pos[s];
+            const int pp = group_min<16>(q);
+#pragma unroll
+            for (int s = 0; s < RPL; ++s) om[s] = __builtin_amdgcn_ballot_w64(pos[s] == pp);
         }
         bool own[RPL];
 #pragma unroll
-        for (int s = 0; s < RPL; ++s) own[s] = unique ? hit[s] : pos[s] == pp;
+        for (int s = 0; s < RPL; ++s) own[s] = __builtin_amdgcn_inverse_ballot_w64(om[s]);
 
         // the owner publishes its row (A chunks from the one holding column
         // j, then B) and where it came from
@@ -344,28 +361,23 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
         const float piv = bcast<J4>(ch[j % 4]);
         const float pm = __builtin_fabsf(piv);
         const bool zero = pm == 0.0f;
-        if (zero && info == 0 && j < n) info = j + 1;
+        wave_zero |= __builtin_amdgcn_ballot_w64(zero) != 0;
         float r = recip_step(piv);
         rd[j] = r;
         const bool small = !(pm >= O::sfmin());
-        if (small) smallmask |= 1u << j;
+        wave_small |= __builtin_amdgcn_ballot_w64(small) != 0;
         // every row of the matrix is updated (rows already chosen get values
         // that are never used); a zero pivot skips the step for its matrix
+        const bool step_small = __builtin_amdgcn_ballot_w64(small && !zero) != 0;
         if (!zero) {
             // multipliers l = a * r; a / pivot where the pivot is below the
-            // smallest normal
-            float q[RPL];
-            const bool anysmall = __builtin_amdgcn_ballot_w64(small) != 0;
-            if (anysmall) {
+            // smallest normal (a branch of its own: rare)
+            if (step_small) {
 #pragma unroll
-                for (int s = 0; s < RPL; ++s) q[s] = a[s][j] / piv;
-            }
+                for (int s = 0; s < RPL; ++s) a[s][j] = small ? a[s][j] / piv : a[s][j] * r;
+            } else {
 #pragma unroll
-            for (int s = 0; s < RPL; ++s) a[s][j] = a[s][j] * r;
-            if (anysmall) {
-#pragma unroll
-                for (int s = 0; s < RPL; ++s)
-                    if (small) a[s][j] = q[s];
+                for (int s = 0; s < RPL; ++s) a[s][j] = a[s][j] * r;
             }
             float lm[RPL];
 #pragma unroll
@@ -408,6 +420,16 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
             });
         }
     });
+
+    // info: the first step whose pivot is exactly zero (1-based), read back
+    // from the diagonal of the record when the wavefront met one
+    int info = 0;
+    if (wave_zero) {
+        for (int k = n - 1; k >= 0; --k) {
+            const float* const dk = reinterpret_cast<const float*>(rbase + rec_off_dyn<NBC, NRC>(k)) + (k & 3);
+            if (*dk == 0.0f) info = k + 1;
+        }
+    }
 
     // ---- L, U and ipiv out ------------------------------------------------------
     // Each row leaves from the lane that held it, to its final position: the
@@ -459,7 +481,7 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
             const int rc = li < NR ? li : NR - 1;
             const float* const yb = reinterpret_cast<const float*>(rbase) + rc;
             float x[NB];
-            const bool fast = n == NB && __builtin_amdgcn_ballot_w64(smallmask != 0) == 0;
+            const bool fast = n == NB && !wave_small;
             if (fast) {
                 static_for<0, NB>([&](auto ic) {
                     constexpr int k = NB - 1 - decltype(ic)::value;
@@ -494,7 +516,7 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
                         const uint4 w = rbase[RO + k / 4];
                         const float u[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
                                             __uint_as_float(w.w)};
-                        if ((smallmask >> k) & 1u)
+                        if (!(__builtin_fabsf(u[k % 4]) >= O::sfmin()))
                             x[k] = acc / u[k % 4];
                         else
                             x[k] = acc * rd[k];
