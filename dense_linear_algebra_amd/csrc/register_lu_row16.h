@@ -328,22 +328,32 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
         for (int s = 0; s < RPL; ++s) own[s] = __builtin_amdgcn_inverse_ballot_w64(om[s]);
 
         // the owner publishes its row (A chunks from the one holding column
-        // j, then B) and where it came from
+        // j, then B) and where it came from.  The row is first selected from
+        // the owner's slot into fresh registers, which the compiler places as
+        // aligned quads: one 16-byte store per chunk from one exec region
+        // (LDS instructions, not bytes, are what the LDS pipe pays for).
+        {
+            bool anyown = own[0];
+            int opos = pos[0];
+            float t[NB + 4 * NRC];
 #pragma unroll
-        for (int s = 0; s < RPL; ++s) {
-            if (own[s]) {
-                const uint32_t ra = lds_rec + 16u * (RO + J4);   // start of record row j
-                static_for<0, NB / 2 - 2 * J4>([&](auto kc) {
-                    constexpr int e = 2 * decltype(kc)::value;
-                    ds_write2<e, e + 1>(ra, a[s][4 * J4 + e], a[s][4 * J4 + e + 1]);
-                });
-                if constexpr (NRC > 0) {
-                    static_for<0, 2 * NRC>([&](auto rc) {
-                        constexpr int e = 2 * decltype(rc)::value;
-                        ds_write2<NB - 4 * J4 + e, NB - 4 * J4 + e + 1>(ra, b[s][e], b[s][e + 1]);
-                    });
-                }
-                *ppos_g = pos[s];
+            for (int k = 4 * J4; k < NB; ++k) t[k] = a[0][k];
+#pragma unroll
+            for (int r2 = 0; r2 < 4 * NRC; ++r2) t[NB + r2] = b[0][r2];
+            if constexpr (RPL == 2) {
+                anyown = own[0] || own[1];
+                opos = own[1] ? pos[1] : pos[0];
+#pragma unroll
+                for (int k = 4 * J4; k < NB; ++k) t[k] = own[1] ? a[1][k] : t[k];
+#pragma unroll
+                for (int r2 = 0; r2 < 4 * NRC; ++r2) t[NB + r2] = own[1] ? b[1][r2] : t[NB + r2];
+            }
+            if (anyown) {
+#pragma unroll
+                for (int c = J4; c < ROWC; ++c)
+                    rbase[RO + c] = make_uint4(__float_as_uint(t[4 * c]), __float_as_uint(t[4 * c + 1]),
+                                               __float_as_uint(t[4 * c + 2]), __float_as_uint(t[4 * c + 3]));
+                *ppos_g = opos;
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
