@@ -179,7 +179,7 @@ __device__ inline bool recip_fast_ok(float ax) { return ax >= 0x1p-125f && ax <=
 __device__ inline float recip_step(float piv) {
     float r = recip_fast(piv);
     const bool ok = recip_fast_ok(__builtin_fabsf(piv));
-    if (__builtin_amdgcn_ballot_w64(!ok) != 0) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!ok) != 0, 0)) {
         asm volatile("" ::: "memory");
         if (!ok) r = 1.0f / piv;
     }
@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
             both &= om[s];
         }
         const bool unique = __builtin_popcountll(hits) == 4 && (RPL == 1 || both == 0);
-        if (!unique) {
+        if (__builtin_expect(!unique, 0)) {
             int q = 0x7fffffff;
 #pragma unroll
             for (int s = 0; s < RPL; ++s)
@@ -381,13 +381,17 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
         const bool step_small = __builtin_amdgcn_ballot_w64(small && !zero) != 0;
         if (!zero) {
             // multipliers l = a * r; a / pivot where the pivot is below the
-            // smallest normal (a branch of its own: rare)
-            if (step_small) {
+            // smallest normal (rare: a fix-up off the straight path)
+            float a0[RPL];
 #pragma unroll
-                for (int s = 0; s < RPL; ++s) a[s][j] = small ? a[s][j] / piv : a[s][j] * r;
-            } else {
+            for (int s = 0; s < RPL; ++s) {
+                a0[s] = a[s][j];
+                a[s][j] = a0[s] * r;
+            }
+            if (__builtin_expect(step_small, 0)) {
 #pragma unroll
-                for (int s = 0; s < RPL; ++s) a[s][j] = a[s][j] * r;
+                for (int s = 0; s < RPL; ++s)
+                    if (small) a[s][j] = a0[s] / piv;
             }
             float lm[RPL];
 #pragma unroll
@@ -493,20 +497,35 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
             float x[NB];
             const bool fast = n == NB && !wave_small;
             if (fast) {
+                // U row k is read one row ahead into a second register set;
+                // each dot product runs as four partial sums (one per element
+                // of a chunk), so the chains stay short
+                uint4 ub[2][NBC];
+                float yv[2];
+                auto load_row = [&](auto kc, auto bc) {
+                    constexpr int k = decltype(kc)::value;
+                    constexpr int bsel = decltype(bc)::value;
+                    constexpr int RO = rec_off<NBC, NRC>(k) - k / 4;
+#pragma unroll
+                    for (int c = k / 4; c < NBC; ++c) ub[bsel][c] = rbase[RO + c];
+                    yv[bsel] = yb[4 * (RO + NBC)];
+                };
+                load_row(std::integral_constant<int, NB - 1>{}, std::integral_constant<int, (NB - 1) & 1>{});
                 static_for<0, NB>([&](auto ic) {
                     constexpr int k = NB - 1 - decltype(ic)::value;
-                    constexpr int RO = rec_off<NBC, NRC>(k) - k / 4;
-                    float acc = yb[4 * (RO + NBC)];
+                    constexpr int bsel = k & 1;
+                    if constexpr (k > 0)
+                        load_row(std::integral_constant<int, k - 1>{}, std::integral_constant<int, (k - 1) & 1>{});
+                    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int c = NBC - 1; c >= k / 4; --c) {
-                        const uint4 w = rbase[RO + c];
-                        const float u[4] = {__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z),
-                                            __uint_as_float(w.w)};
+                        const float u[4] = {__uint_as_float(ub[bsel][c].x), __uint_as_float(ub[bsel][c].y),
+                                            __uint_as_float(ub[bsel][c].z), __uint_as_float(ub[bsel][c].w)};
 #pragma unroll
                         for (int t = 3; t >= 0; --t)
-                            if (4 * c + t > k) acc = __builtin_fmaf(-u[t], x[4 * c + t], acc);
+                            if (4 * c + t > k) ps[t] = __builtin_fmaf(u[t], x[4 * c + t], ps[t]);
                     }
-                    x[k] = acc * rd[k];
+                    x[k] = (yv[bsel] - ((ps[0] + ps[1]) + (ps[2] + ps[3]))) * rd[k];
                 });
             } else {
                 static_for<0, NB>([&](auto ic) {
