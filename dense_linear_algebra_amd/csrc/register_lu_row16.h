@@ -302,6 +302,13 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
             kmax = kk > kmax ? kk : kmax;
         }
         kmax = group_max16_i32(kmax);
+        // |pivot| is the winning key (a NaN for the clamped key): the
+        // reciprocal of the magnitude starts here, off the LDS round trip;
+        // the sign arrives with the published row (1/(-x) = -(1/x) exactly)
+        const float pm = __uint_as_float((uint32_t)kmax);
+        const bool zero = pm == 0.0f;
+        const bool small = !(pm >= O::sfmin());
+        const float rabs = recip_step(pm);
         // one maximal row per matrix (the usual case) needs no position
         // reduction; otherwise the lowest position among the maximal wins.
         // Ownership stays in scalar lane masks.
@@ -369,12 +376,9 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
         for (int s = 0; s < RPL; ++s) pos[s] = own[s] ? j : (pos[s] == j ? piv_pos : pos[s]);
 
         const float piv = bcast<J4>(ch[j % 4]);
-        const float pm = __builtin_fabsf(piv);
-        const bool zero = pm == 0.0f;
         wave_zero |= __builtin_amdgcn_ballot_w64(zero) != 0;
-        float r = recip_step(piv);
+        const float r = __uint_as_float(__float_as_uint(rabs) ^ (__float_as_uint(piv) & 0x80000000u));
         rd[j] = r;
-        const bool small = !(pm >= O::sfmin());
         wave_small |= __builtin_amdgcn_ballot_w64(small) != 0;
         // every row of the matrix is updated (rows already chosen get values
         // that are never used); a zero pivot skips the step for its matrix
