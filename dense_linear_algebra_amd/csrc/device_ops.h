@@ -251,7 +251,7 @@ __device__ inline void wave_argmax(uint32_t key, int pos, uint32_t& kmax, int& w
     if (kmax == 0) return;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(key == kmax);
     win = __builtin_ctzll(hit);
-    if (__builtin_popcountll(hit) != 1) tie_break(key == kmax, pos, win);
+    if (__builtin_expect(__builtin_popcountll(hit) != 1, 0)) tie_break(key == kmax, pos, win);
 }
 // 64-bit keys: the high words decide unless several lanes share the maximal
 // high word; only then are the low words reduced
@@ -260,7 +260,7 @@ __device__ inline void wave_argmax(uint64_t key, int pos, uint64_t& kmax, int& w
     const uint32_t mh = wave_max(hi);
     uint64_t hit = __builtin_amdgcn_ballot_w64(hi == mh);
     win = -1;
-    if (mh != 0 && __builtin_popcountll(hit) == 1) {
+    if (__builtin_expect(mh != 0 && __builtin_popcountll(hit) == 1, 1)) {
         win = __builtin_ctzll(hit);
         kmax = ((uint64_t)mh << 32) | (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, win);
         return;
@@ -270,7 +270,7 @@ __device__ inline void wave_argmax(uint64_t key, int pos, uint64_t& kmax, int& w
     if (kmax == 0) return;
     hit = __builtin_amdgcn_ballot_w64(key == kmax);
     win = __builtin_ctzll(hit);
-    if (__builtin_popcountll(hit) != 1) tie_break(key == kmax, pos, win);
+    if (__builtin_expect(__builtin_popcountll(hit) != 1, 0)) tie_break(key == kmax, pos, win);
 }
 
 

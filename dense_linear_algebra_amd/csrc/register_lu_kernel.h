@@ -160,12 +160,22 @@ register_lu_kernel(Problem p, int mode)
             key[s] = kk;
             kmax = kk > kmax ? kk : kmax;
         }
-        kmax = group_max<LPM>(kmax);
-        int q = 0x7fffffff;
+        int piv_pos;
+        if constexpr (LPM == 64) {
+            // one matrix per wavefront (one row per lane): DPP inside rows
+            // of 16 lanes and readlane across them, no LDS round trips; the
+            // position reduction runs only when several rows share the key
+            int win;
+            wave_argmax(key[0], pos[0], kmax, win);
+            piv_pos = __builtin_amdgcn_readlane(pos[0], win < 0 ? 0 : win);
+        } else {
+            kmax = group_max<LPM>(kmax);
+            int q = 0x7fffffff;
 #pragma unroll
-        for (int s = 0; s < RPL; ++s)
-            if (key[s] == kmax && pos[s] < q) q = pos[s];
-        const int piv_pos = group_min<LPM>(q);
+            for (int s = 0; s < RPL; ++s)
+                if (key[s] == kmax && pos[s] < q) q = pos[s];
+            piv_pos = group_min<LPM>(q);
+        }
         if (li == j % LPM) pivrec[j / LPM] = piv_pos;
 
         // publish the pivot row (chunks from the one holding column j)
@@ -247,7 +257,7 @@ register_lu_kernel(Problem p, int mode)
         T lm[RPL];
 #pragma unroll
         for (int s = 0; s < RPL; ++s) lm[s] = O::mul(a[s][j], r);
-        if (__builtin_amdgcn_ballot_w64(small) != 0) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(small) != 0, 0)) {
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int s = 0; s < RPL; ++s)
@@ -332,7 +342,7 @@ register_lu_kernel(Problem p, int mode)
                 const T rk = diag[2 * k];
                 const T dk = diag[2 * k + 1];
                 const bool tiny = !(O::metric(dk) >= O::sfmin());
-                if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
+                if (__builtin_expect(__builtin_amdgcn_ballot_w64(tiny) != 0, 0)) {
                     asm volatile("" ::: "memory");
 #pragma unroll
                     for (int r2 = 0; r2 < NR; ++r2) xk[r2] = tiny ? O::div(xk[r2], dk) : O::mul(xk[r2], rk);
