@@ -138,7 +138,7 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
             K kmax;
             int win;
             wave_argmax(key, pos, kmax, win);
-            if (win < 0) {
+            if (__builtin_expect(win < 0, 0)) {
                 // no candidate row in this wavefront
                 if (lane == 0) {
                     skey[buf][wave] = 0;
@@ -196,7 +196,7 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
             pos = (pos == ppos) ? jj : (pos == jj ? ppos : pos);
             const R pm = O::metric(piv);
             const bool zero = pm == R(0);
-            if (zero) {
+            if (__builtin_expect(zero, 0)) {
                 zmask |= 1u << jj;
                 if (info == 0) info = j0 + jj + 1;
             }
@@ -208,7 +208,7 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
             // search); f64 masks (a select costs two instructions there)
             const bool upd = pos > jj && pos < m && !zero;
             T l = O::mul(a[jj], r);
-            if (__builtin_amdgcn_ballot_w64(small && upd) != 0) {
+            if (__builtin_expect(__builtin_amdgcn_ballot_w64(small && upd) != 0, 0)) {
                 asm volatile("" ::: "memory");
                 if (small && upd) l = O::div(a[jj], piv);
             }

@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(MAXT) panel_kernel(Problem p, int j0, int w)
         for (int q = 0; q < RPT; ++q) {
             if (pos[q] > jj && pos[q] < m && !zero) {
                 T l = O::mul(a[q][jj], r);
-                if (__builtin_amdgcn_ballot_w64(small) != 0) {
+                if (__builtin_expect(__builtin_amdgcn_ballot_w64(small) != 0, 0)) {
                     asm volatile("" ::: "memory");
                     if (small) l = O::div(a[q][jj], piv);
                 }
@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(256) panel4_kernel(Problem p, int j0, int w)
         K kmax;
         int win;
         wave_argmax(key, kp, kmax, win);
-        if (win < 0) {
+        if (__builtin_expect(win < 0, 0)) {
             if (lane == 0) {
                 skey[buf][wave] = 0;
                 spos[buf][wave] = 0x7fffffff;
@@ -294,7 +294,7 @@ __global__ void __launch_bounds__(256) panel4_kernel(Problem p, int j0, int w)
         for (int q = 0; q < RPT; ++q) {
             if (pos[q] > jj && pos[q] < m && !zero) {
                 T l = O::mul(a[q][jj], r);
-                if (__builtin_amdgcn_ballot_w64(small) != 0) {
+                if (__builtin_expect(__builtin_amdgcn_ballot_w64(small) != 0, 0)) {
                     asm volatile("" ::: "memory");
                     if (small) l = O::div(a[q][jj], piv);
                 }
