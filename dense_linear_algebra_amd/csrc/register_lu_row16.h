@@ -33,7 +33,7 @@ namespace batchlu {
 
 namespace row16_detail {
 
-constexpr int kWaves = 4;   // wavefronts per block
+constexpr int kWaves = 2;   // wavefronts per block (smaller blocks even out the end of the grid)
 
 // row_newbcast:L broadcasts lane L of every 16-lane row to the whole row
 template <int L>
