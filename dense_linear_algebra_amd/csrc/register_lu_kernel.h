@@ -161,13 +161,18 @@ register_lu_kernel(Problem p, int mode)
             kmax = kk > kmax ? kk : kmax;
         }
         int piv_pos;
+        T piv_early = O::zero();
         if constexpr (LPM == 64) {
             // one matrix per wavefront (one row per lane): DPP inside rows
             // of 16 lanes and readlane across them, no LDS round trips; the
-            // position reduction runs only when several rows share the key
+            // position reduction runs only when several rows share the key.
+            // The pivot itself is read from the winning lane here, so that
+            // its reciprocal does not wait for the pivot row's round trip.
             int win;
             wave_argmax(key[0], pos[0], kmax, win);
-            piv_pos = __builtin_amdgcn_readlane(pos[0], win < 0 ? 0 : win);
+            win = win < 0 ? 0 : win;
+            piv_pos = __builtin_amdgcn_readlane(pos[0], win);
+            piv_early = readlane_t(a[0][j], win);
         } else {
             kmax = group_max<LPM>(kmax);
             int q = 0x7fffffff;
@@ -237,7 +242,7 @@ register_lu_kernel(Problem p, int mode)
             __builtin_memcpy(&u[(j / CH) * CH], &w, 16);
         }
 
-        const T piv = u[j];
+        const T piv = (LPM == 64) ? piv_early : u[j];
         const R pm = O::metric(piv);
         const bool zero = (pm == R(0));
         if (zero && info == 0) info = j + 1;
