@@ -156,7 +156,9 @@ register_lu_kernel(Problem p, int mode)
         K kmax = 0;
 #pragma unroll
         for (int s = 0; s < RPL; ++s) {
-            K kk = (pos[s] >= j) ? (K)pivot_key(O::metric(a[s][j])) : (K)0;
+            // rows past n pad the bucket; never candidates (0 * inf in their
+            // updates can make them NaN, which would outrank real rows)
+            K kk = (pos[s] >= j && pos[s] < n) ? (K)pivot_key(O::metric(a[s][j])) : (K)0;
             key[s] = kk;
             kmax = kk > kmax ? kk : kmax;
         }

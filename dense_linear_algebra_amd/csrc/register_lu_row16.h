@@ -297,7 +297,9 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
 #pragma unroll
         for (int s = 0; s < RPL; ++s) {
             const uint32_t bits = __float_as_uint(a[s][j]) & 0x7fffffffu;
-            const int kk = (pos[s] >= j) ? (int)(bits < 0x7f800001u ? bits : 0x7f800001u) : -1;
+            // rows past n pad the bucket and are never candidates (0 * inf in
+            // their updates can make them NaN, which would outrank real rows)
+            const int kk = (pos[s] >= j && pos[s] < n) ? (int)(bits < 0x7f800001u ? bits : 0x7f800001u) : -1;
             key[s] = kk;
             kmax = kk > kmax ? kk : kmax;
         }

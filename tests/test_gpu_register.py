@@ -195,3 +195,48 @@ def test_full_size_workloads(name):
 def test_selected_tiers():
     assert lib.batchlu_select_tier(lib.R32, 2, 32, 8, 32768) == lib.TIER_TINY
     assert lib.batchlu_select_tier(lib.C64, 2, 64, 16, 8192) == lib.TIER_CTA
+
+
+EXTREME = ([(np.float32, n) for n in (16, 20, 32, 48, 64, 100, 256)]
+           + [(np.float64, n) for n in (17, 32, 64, 256)]
+           + [(np.complex64, n) for n in (24, 64)])
+
+
+@pytest.mark.parametrize("dtype,n", EXTREME)
+def test_extreme_pivot_scales(dtype, n):
+    """Pivots below the smallest normal (multipliers and back substitution by
+    true division), pivots beyond 2^125 (reciprocals outside the range where
+    the fast reciprocal is exact) and a single small pivot inside an
+    otherwise normal matrix, mixed in one batch with normal matrices so that
+    the rare paths run for some matrices of a wavefront only.  ipiv, info
+    and L/U bit-identical to the oracle (infinities from growth included);
+    X within the solve-residual bound for the unscaled matrices."""
+    rng = np.random.default_rng(2000 + n)
+    real = np.float32 if dtype in (np.float32, np.complex64) else np.float64
+    tiny = 2.0 ** (-140 if real == np.float32 else -1035)
+    huge = 2.0 ** (125.5 if real == np.float32 else 1021.5)
+    mats, kinds = [], []
+    for b in range(24):
+        M = rng.uniform(-1, 1, (n, n))
+        if np.iscomplexobj(np.zeros(1, dtype)):
+            M = M + 1j * rng.uniform(-1, 1, (n, n))
+        kind = b % 4
+        if kind == 1:
+            M = M * tiny
+        elif kind == 2:
+            M = M * huge
+        elif kind == 3:
+            M[:, n // 2] *= tiny
+        mats.append(M)
+        kinds.append(kind)
+    batch, nrhs = len(mats), 3
+    A = np.concatenate([_one(M, dtype) for M in mats])
+    B = rng.uniform(-1, 1, batch * n * nrhs).astype(dtype)
+    print(f"case extreme {np.dtype(dtype).name} n={n}", flush=True)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch)
+    oA, oB, oP, oI, _ = oracle_run(A, B, n, nrhs, batch)
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+    normal = [b for b in range(batch) if kinds[b] == 0 and oI[b] == 0]
+    _check_solution(A, B, gB, n, nrhs, batch, oI, oB, sample=normal)
