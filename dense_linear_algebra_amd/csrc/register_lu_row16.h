@@ -186,18 +186,6 @@ __device__ inline float recip_step(float piv) {
     return r;
 }
 
-// two floats into LDS at byte address addr + 4*O0 and addr + 4*O1.  The
-// pivot row is published this way: ds_write2_b32 takes any two registers,
-// where a 16-byte store would need the row's chunks in aligned register
-// quads (a copy per element otherwise).  The clobber keeps later LDS reads
-// after it.
-template <int O0, int O1>
-__device__ inline void ds_write2(uint32_t addr, float x0, float x1) {
-    static_assert(O0 >= 0 && O0 < 256 && O1 >= 0 && O1 < 256, "ds_write2_b32 offsets are 8-bit dword counts");
-    asm volatile("ds_write2_b32 %0, %1, %2 offset0:%3 offset1:%4" ::"v"(addr), "v"(x0), "v"(x1), "n"(O0), "n"(O1)
-                 : "memory");
-}
-
 template <int NB, int NR>
 __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
 {
@@ -279,7 +267,6 @@ __global__ void __launch_bounds__(64 * kWaves) row16_kernel(Problem p, int mode)
     bool wave_small = false;      // some pivot below the smallest normal
     uint4* const rbase = &rec[grp >> 2][(grp & 3) * RSTRIDE];
     int* const ppos_g = &ppos[grp];
-    const uint32_t lds_rec = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)rbase;
     // lane li reads chunk li of each published row (lanes past the row read
     // its first chunk); rec_off(j) - j/4 >= 0 keeps every address in range
     const uint4* const rread = rbase + (li < ROWC ? li : 0);
