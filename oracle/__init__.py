@@ -50,6 +50,9 @@ def _load():
             lib.oracle_getrf_batch.restype = i32
             lib.oracle_getrs_batch.argtypes = [i32, i32, i32, vp, i32, i64, ip, i64, vp, i32, i64, i32, i32]
             lib.oracle_getrs_batch.restype = i32
+            lib.oracle_getrs_trans_batch.argtypes = [i32, i32, i32, i32, vp, i32, i64, ip, i64, vp, i32, i64,
+                                                     i32, i32]
+            lib.oracle_getrs_trans_batch.restype = i32
             lib.oracle_gesv_batch.argtypes = [i32, i32, i32, vp, i32, i64, ip, i64, vp, i32, i64, ip, dp, i32, i32]
             lib.oracle_gesv_batch.restype = i32
             _lib = lib
@@ -92,15 +95,20 @@ def getrf(A, n, lda, strideA, batch, strideP=None, want_margins=False, nthreads=
     return ipiv[:, :max(n, 0)] if strideP == n else ipiv, info, margins, used
 
 
-def getrs(LU, n, lda, strideA, ipiv, B, nrhs, ldb, strideB, batch, nthreads=0):
-    """Solve A X = B in place of ``B`` from the oracle's (or any) LU + ipiv."""
+def getrs(LU, n, lda, strideA, ipiv, B, nrhs, ldb, strideB, batch, nthreads=0, trans="N"):
+    """Solve op(A) X = B in place of ``B`` from the oracle's (or any) LU + ipiv;
+    op is A for trans 'N', A^T for 'T', A^H for 'C' (A^T for real types)."""
     ipiv = np.ascontiguousarray(ipiv, dtype=np.int32).reshape(batch, -1)
+    code = {"N": 0, "T": 1, "C": 2}[trans.upper()]
     if batch > 0 and n > 0 and nrhs > 0:
         _check_flat(B, (batch - 1) * strideB + (nrhs - 1) * ldb + n, "B")
         if LU.dtype != B.dtype:
             raise TypeError("LU and B dtypes differ")
-    return _load().oracle_getrs_batch(_code(B), n, nrhs, _ptr(LU), lda, strideA, _ptr(ipiv), ipiv.shape[1],
-                                      _ptr(B), ldb, strideB, batch, nthreads)
+    if code == 0:
+        return _load().oracle_getrs_batch(_code(B), n, nrhs, _ptr(LU), lda, strideA, _ptr(ipiv), ipiv.shape[1],
+                                          _ptr(B), ldb, strideB, batch, nthreads)
+    return _load().oracle_getrs_trans_batch(_code(B), code, n, nrhs, _ptr(LU), lda, strideA, _ptr(ipiv),
+                                            ipiv.shape[1], _ptr(B), ldb, strideB, batch, nthreads)
 
 
 def gesv(A, n, lda, strideA, B, nrhs, ldb, strideB, batch, want_margins=False, nthreads=0):

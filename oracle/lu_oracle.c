@@ -32,6 +32,12 @@
  *       im = fma(ar, ri, ai*rr).
  *   R5  getrs: x_k = y_k / u_kk (true division), then y_i -= u_ik * x_k.
  *   R6  gesv leaves B untouched for a matrix whose info > 0.
+ *   R7  getrs with op(A) = A^T or A^H (the pages name a Trans solve kernel
+ *       and test every transpose without spelling it out): LAPACK's meaning,
+ *       A^T = U^T L^T P, solved as U^T w = b with true division by u_kk,
+ *       then L^T z = w, then x = P^T z (transpositions in reverse order);
+ *       A^H uses the conjugates of the factors.  Forward sums run in
+ *       ascending k, backward sums in descending k, as in R5.
  *
  * Arithmetic is in the working precision of the data type (the pivot choice
  * must be reproduced exactly); margins are reported in double.  Build with
@@ -146,6 +152,36 @@ void NAME(int n, int nrhs, const T* A, int lda, const int* ipiv,               \
 
 DEFINE_REAL_GETRS(oracle_sgetrs, float, fmaf)
 DEFINE_REAL_GETRS(oracle_dgetrs, double, fma)
+
+/* ------------------------------------------------------------------ */
+/* real getrs (Trans): A = P^T L U, so A^T = U^T L^T P and the solve   */
+/* is U^T w = b (forward, dividing by u_kk), L^T z = w (backward, unit */
+/* diagonal), then x = P^T z: the transpositions in reverse order.     */
+/* Both substitutions accumulate in substitution order, as for NoTrans. */
+/* ------------------------------------------------------------------ */
+#define DEFINE_REAL_GETRS_T(NAME, T, FMA)                                      \
+void NAME(int n, int nrhs, const T* A, int lda, const int* ipiv,               \
+          T* B, int ldb)                                                       \
+{                                                                              \
+    for (int c = 0; c < nrhs; ++c) {                                           \
+        T* b = B + (size_t)c * ldb;                                            \
+        for (int k = 0; k < n; ++k) {       /* U^T w = b: (U^T)_ik = u_ki */   \
+            b[k] = b[k] / A[k + (size_t)k * lda];                              \
+            for (int i = k + 1; i < n; ++i)                                    \
+                b[i] = FMA(-A[k + (size_t)i * lda], b[k], b[i]);               \
+        }                                                                      \
+        for (int k = n - 1; k >= 0; --k)    /* L^T z = w: (L^T)_ik = l_ki */   \
+            for (int i = 0; i < k; ++i)                                        \
+                b[i] = FMA(-A[k + (size_t)i * lda], b[k], b[i]);               \
+        for (int k = n - 1; k >= 0; --k) {  /* x = P^T z */                    \
+            int p = ipiv[k] - 1;                                               \
+            if (p != k) { T t = b[k]; b[k] = b[p]; b[p] = t; }                 \
+        }                                                                      \
+    }                                                                          \
+}
+
+DEFINE_REAL_GETRS_T(oracle_sgetrs_t, float, fmaf)
+DEFINE_REAL_GETRS_T(oracle_dgetrs_t, double, fma)
 
 /* ------------------------------------------------------------------ */
 /* complex helpers (interleaved re, im), every operation rounded once  */
@@ -269,6 +305,37 @@ void oracle_##PFX##getrs(int n, int nrhs, const T* A, int lda,                 \
                 PFX##_fms(b + 2 * i, A + 2 * (i + (size_t)k * lda), b + 2 * k);\
         }                                                                      \
     }                                                                          \
+}                                                                              \
+void oracle_##PFX##getrs_t(int n, int nrhs, const T* A, int lda,               \
+                           const int* ipiv, T* B, int ldb, int conj)           \
+{                                                                              \
+    const T sg = conj ? (T)-1 : (T)1;   /* 'C' uses conj(u_ki), conj(l_ki) */  \
+    for (int c = 0; c < nrhs; ++c) {                                           \
+        T* b = B + 2 * (size_t)c * ldb;                                        \
+        for (int k = 0; k < n; ++k) {                                          \
+            const T* u = A + 2 * (k + (size_t)k * lda);                        \
+            PFX##_div(b[2 * k], b[2 * k + 1], u[0], sg * u[1], b + 2 * k);     \
+            for (int i = k + 1; i < n; ++i) {                                  \
+                const T* e = A + 2 * (k + (size_t)i * lda);                    \
+                T x[2] = {e[0], sg * e[1]};                                    \
+                PFX##_fms(b + 2 * i, x, b + 2 * k);                            \
+            }                                                                  \
+        }                                                                      \
+        for (int k = n - 1; k >= 0; --k)                                       \
+            for (int i = 0; i < k; ++i) {                                      \
+                const T* e = A + 2 * (k + (size_t)i * lda);                    \
+                T x[2] = {e[0], sg * e[1]};                                    \
+                PFX##_fms(b + 2 * i, x, b + 2 * k);                            \
+            }                                                                  \
+        for (int k = n - 1; k >= 0; --k) {                                     \
+            int p = ipiv[k] - 1;                                               \
+            if (p != k)                                                        \
+                for (int h = 0; h < 2; ++h) {                                  \
+                    T t = b[2 * k + h]; b[2 * k + h] = b[2 * p + h];           \
+                    b[2 * p + h] = t;                                          \
+                }                                                              \
+        }                                                                      \
+    }                                                                          \
 }
 
 DEFINE_COMPLEX_GETRF_GETRS(c, float, fmaf, fabsf, FLT_MIN)
@@ -290,6 +357,7 @@ static size_t elem_size(int t)
 
 typedef struct {
     int op;            /* 0 getrf, 1 getrs, 2 gesv */
+    int trans;         /* getrs only: 0 A, 1 A^T, 2 A^H */
     int t, n, nrhs;
     char* A; int lda; long long sA;
     int* ipiv; long long sP;
@@ -320,6 +388,17 @@ static void one_getrs(const job_t* J, int b)
     const void* A = J->A + (size_t)b * J->sA * es;
     const int* ip = J->ipiv + (size_t)b * J->sP;
     void* B = J->B + (size_t)b * J->sB * es;
+    if (J->trans) {
+        switch (J->t) {
+        case OR_R32: oracle_sgetrs_t(J->n, J->nrhs, (const float*)A, J->lda, ip, (float*)B, J->ldb); break;
+        case OR_R64: oracle_dgetrs_t(J->n, J->nrhs, (const double*)A, J->lda, ip, (double*)B, J->ldb); break;
+        case OR_C64: oracle_cgetrs_t(J->n, J->nrhs, (const float*)A, J->lda, ip, (float*)B, J->ldb,
+                                     J->trans == 2); break;
+        case OR_C128: oracle_zgetrs_t(J->n, J->nrhs, (const double*)A, J->lda, ip, (double*)B, J->ldb,
+                                      J->trans == 2); break;
+        }
+        return;
+    }
     switch (J->t) {
     case OR_R32: oracle_sgetrs(J->n, J->nrhs, (const float*)A, J->lda, ip, (float*)B, J->ldb); break;
     case OR_R64: oracle_dgetrs(J->n, J->nrhs, (const double*)A, J->lda, ip, (double*)B, J->ldb); break;
@@ -379,6 +458,18 @@ int oracle_getrs_batch(int t, int n, int nrhs, const void* A, int lda,
 {
     job_t J; memset(&J, 0, sizeof J);
     J.op = 1; J.t = t; J.n = n; J.nrhs = nrhs; J.A = (char*)A; J.lda = lda;
+    J.sA = strideA; J.ipiv = (int*)ipiv; J.sP = strideP; J.B = (char*)B;
+    J.ldb = ldb; J.sB = strideB;
+    return run_batch(J, batch, nthreads);
+}
+
+/* trans: 0 solves A X = B, 1 solves A^T X = B, 2 solves A^H X = B */
+int oracle_getrs_trans_batch(int t, int trans, int n, int nrhs, const void* A, int lda,
+                             long long strideA, const int* ipiv, long long strideP,
+                             void* B, int ldb, long long strideB, int batch, int nthreads)
+{
+    job_t J; memset(&J, 0, sizeof J);
+    J.op = 1; J.trans = trans; J.t = t; J.n = n; J.nrhs = nrhs; J.A = (char*)A; J.lda = lda;
     J.sA = strideA; J.ipiv = (int*)ipiv; J.sP = strideP; J.B = (char*)B;
     J.ldb = ldb; J.sB = strideB;
     return run_batch(J, batch, nthreads);

@@ -361,6 +361,50 @@ def test_solve_against_lapack(dtype, n, nrhs):
         assert err <= 64 * n * oracle.eps_of(dtype) * cond
 
 
+def test_integer_transposed_solve_is_exact():
+    """A^T x = b and A^H x = b with a unimodular integer matrix whose
+    factorisation swaps rows: exact in double, so undoing the interchanges in
+    the wrong order, or taking L^T / U^T from the wrong triangle, fails."""
+    A = np.array([[2, 1, 0, 0], [4, 3, 1, 0], [0, 2, 2, 1], [0, 0, 4, 3]], np.float64)
+    x = np.array([[1, -2], [3, 0], [-1, 5], [2, 1]], np.float64)
+    flatA = _flat_colmajor(A)
+    ipiv, info, _, _ = oracle.getrf(flatA, 4, 4, 16, 1)
+    assert info[0] == 0 and list(ipiv[0]) != [1, 2, 3, 4]
+    for trans in ("T", "C"):
+        flatB = _flat_colmajor(A.T @ x)
+        oracle.getrs(flatA, 4, 4, 16, ipiv, flatB, 2, 4, 8, 1, trans=trans)
+        np.testing.assert_allclose(oracle.matrix(flatB, 0, 4, 2, 4, 8), x, rtol=0, atol=1e-14)
+    Ac = A + 1j * np.array([[0, 1, 0, 0], [1, 0, 0, 0], [0, 0, 1, 0], [0, 1, 0, 2]])
+    xc = x + 1j * x[::-1]
+    flatA = _flat_colmajor(Ac.astype(np.complex128))
+    ipiv, info, _, _ = oracle.getrf(flatA, 4, 4, 16, 1)
+    assert info[0] == 0
+    for trans, op in (("T", Ac.T), ("C", Ac.conj().T)):
+        flatB = _flat_colmajor(op @ xc)
+        oracle.getrs(flatA, 4, 4, 16, ipiv, flatB, 2, 4, 8, 1, trans=trans)
+        np.testing.assert_allclose(oracle.matrix(flatB, 0, 4, 2, 4, 8), xc, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64, np.complex64, np.complex128])
+@pytest.mark.parametrize("n,nrhs", [(5, 1), (40, 3)])
+@pytest.mark.parametrize("trans", ["T", "C"])
+def test_transposed_solve_against_lapack(dtype, n, nrhs, trans):
+    A_all, B_all = lu_inputs.random_problem(808 + n, dtype, n, nrhs, 3)
+    fa, fb = A_all.copy(), B_all.copy()
+    ipiv, info, _, _ = oracle.getrf(fa, n, n, n * n, 3)
+    oracle.getrs(fa, n, n, n * n, ipiv, fb, nrhs, n, n * nrhs, 3, trans=trans)
+    wide = np.complex128 if np.iscomplexobj(A_all) else np.float64
+    for b in range(3):
+        A = oracle.matrix(A_all, b, n, n, n, n * n).astype(wide)
+        op = A.T if trans == "T" else A.conj().T
+        B = oracle.matrix(B_all, b, n, nrhs, n, n * nrhs).astype(wide)
+        X = oracle.matrix(fb, b, n, nrhs, n, n * nrhs)
+        assert info[b] == 0
+        Xref = np.linalg.solve(op, B)
+        err = np.max(np.abs(X - Xref)) / np.max(np.abs(Xref))
+        assert err <= 64 * n * oracle.eps_of(dtype) * np.linalg.cond(op)
+
+
 def test_gesv_leaves_b_for_singular_matrix():
     A = np.array([[1, 2], [2, 4]], np.float32)
     B = np.array([[3.0], [7.0]], np.float32)
