@@ -130,16 +130,18 @@ int batchlu_getrs(batchlu_dtype t, char trans, int n, int nrhs, const void* A, i
     if (batch > 1 && strideA < (long long)lda * n) return -7;
     if (batch > 1 && strideP < n) return -9;
     if (batch > 1 && strideB < (long long)ldb * nrhs) return -12;
-    if (trans != 'N' && trans != 'n') return BATCHLU_ERR_UNSUPPORTED;
+    const int op = (trans == 'N' || trans == 'n') ? 0 : (trans == 'T' || trans == 't') ? 1 : 2;
     if (n == 0 || nrhs == 0 || batch == 0) return BATCHLU_OK;
     if (!A) return -5;
     if (!ipiv) return -8;
     if (!B) return -10;
+    if (op != 0 && !getrs_rows_supported(t, n)) return BATCHLU_ERR_UNSUPPORTED;   // n > 1024
     const int tier = choose(t, OP_GETRS, n, nrhs);
     if (tier < 0) return tier;
     Problem p;
     p.n = n; p.nrhs = nrhs; p.batch = batch; p.A = const_cast<void*>(A); p.lda = lda; p.sA = strideA;
     p.ipiv = const_cast<int*>(ipiv); p.sP = strideP; p.B = B; p.ldb = ldb; p.sB = strideB;
+    p.trans = op;
     return run_getrs(tier, t, p, stream);
 }
 

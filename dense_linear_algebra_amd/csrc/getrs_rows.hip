@@ -1,5 +1,6 @@
 // getrs_rows.hip -- the whole LU solve of one matrix and one tile of
-// right-hand sides in a single work-group: one row per thread, n <= 1024.
+// right-hand sides in a single work-group: one row per thread, n <= 1024,
+// for A X = B and (second kernel, below) A^T X = B and A^H X = B.
 //
 // BatchLAS "LU" page, fused getrs paragraph (one work-group per matrix does
 // the permutation and both substitutions in one launch) and blocked getrs
@@ -175,13 +176,185 @@ __global__ void __launch_bounds__(1024) getrs_rows_kernel(Problem p, int rtiles)
             if (c0 + r < p.nrhs) B[row + (long long)(c0 + r) * p.ldb] = y[r];
 }
 
+// op(A) = A^T (CONJ false) or A^H (CONJ true).  With A = P^T L U,
+// A^T = U^T L^T P: forward against U^T (lower, true division by u_kk),
+// back against L^T (unit upper), then x = P^T z.  Row `row` of U^T and L^T
+// is column `row` of the stored factors, so each thread walks its own
+// column.  The interchanges are undone by a scatter: z_row goes to row
+// src(row), the same backward trace that the NoTrans gather uses (P b has
+// b_src at row `row`, so P^T z has z_row at row src).  B is read at the
+// start and written at the end, with barriers between, so the scatter needs
+// no second buffer.
+template <bool CONJ, typename T>
+__device__ inline T op_entry(const T& v) {
+    if constexpr (CONJ && ops<T>::is_complex) return T{v.re, -v.im};
+    else return v;
+}
+
+template <typename T, int NRT, bool CONJ>
+__global__ void __launch_bounds__(1024) getrs_rows_trans_kernel(Problem p, int rtiles)
+{
+    using O = ops<T>;
+    extern __shared__ uint4 smem_raw[];
+    int* sipiv = (int*)smem_raw;                                             // n entries
+    T* ybuf = (T*)((char*)smem_raw + ((p.n * 4 + 15) / 16) * 16);            // [2][BS][NRT]
+
+    const int n = p.n;
+    const long long m = blockIdx.x / rtiles;
+    const int c0 = (int)(blockIdx.x % rtiles) * NRT;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    const T* LU = (const T*)p.A + m * p.sA;
+    const int* ipiv = p.ipiv + m * p.sP;
+    T* B = (T*)p.B + m * p.sB;
+
+    for (int i = tid; i < n; i += blockDim.x) {
+        const int v = ipiv[i] - 1;
+        sipiv[i] = (v >= 0 && v < n) ? v : i;
+    }
+    __syncthreads();
+
+    const int row = tid;
+    const bool have = row < n;
+    int dst = row;   // row of X that receives z_row
+    if (have)
+        for (int k = n - 1; k >= 0; --k) {
+            const int pk = sipiv[k];
+            dst = (dst == k) ? pk : (dst == pk ? k : dst);
+        }
+    T y[NRT];
+#pragma unroll
+    for (int r = 0; r < NRT; ++r)
+        y[r] = (have && c0 + r < p.nrhs) ? B[row + (long long)(c0 + r) * p.ldb] : O::zero();
+    const T* col = LU + (long long)row * p.lda;   // column `row`: row `row` of U^T and L^T
+
+    const int P = (n + BS - 1) / BS;
+    // U^T w = b, blocks ascending
+    for (int kb = 0; kb < P; ++kb) {
+        const int r0 = kb * BS;
+        const int w = min(BS, n - r0);
+        T* yb = ybuf + (size_t)(kb & 1) * BS * NRT;
+        if (wave == r0 / 64) {
+            const int base = r0 % 64;
+            const int mrow = lane - base;
+#pragma unroll
+            for (int cc = 0; cc < BS; cc += CK) {
+                T urow[CK];   // (U^T)_{mrow,c} = u_{c,mrow}, diagonal included
+#pragma unroll
+                for (int e = 0; e < CK; ++e) {
+                    const int c = cc + e;
+                    urow[e] = (mrow >= c && mrow < w) ? op_entry<CONJ>(col[r0 + c]) : O::zero();
+                }
+#pragma unroll
+                for (int e = 0; e < CK; ++e) {
+                    const int c = cc + e;
+                    if (c >= w) continue;
+                    if (mrow == c)
+#pragma unroll
+                        for (int r = 0; r < NRT; ++r) y[r] = O::div(y[r], urow[e]);
+                    T xc[NRT];
+#pragma unroll
+                    for (int r = 0; r < NRT; ++r) xc[r] = readlane_t(y[r], base + c);
+                    if (mrow > c && mrow < w)
+#pragma unroll
+                        for (int r = 0; r < NRT; ++r) O::fms(y[r], urow[e], xc[r]);
+                }
+            }
+            if (mrow >= 0 && mrow < w)
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) yb[mrow * NRT + r] = y[r];
+        }
+        __syncthreads();
+        if (have && row >= r0 + w) {
+#pragma unroll
+            for (int cc = 0; cc < BS; cc += CK) {
+                T urow[CK];
+#pragma unroll
+                for (int e = 0; e < CK; ++e)
+                    urow[e] = cc + e < w ? op_entry<CONJ>(col[r0 + cc + e]) : O::zero();
+#pragma unroll
+                for (int e = 0; e < CK; ++e) {
+                    if (cc + e >= w) continue;
+#pragma unroll
+                    for (int r = 0; r < NRT; ++r) O::fms(y[r], urow[e], yb[(cc + e) * NRT + r]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // L^T z = w (unit diagonal), blocks descending
+    for (int kb = P - 1; kb >= 0; --kb) {
+        const int r0 = kb * BS;
+        const int w = min(BS, n - r0);
+        T* yb = ybuf + (size_t)(kb & 1) * BS * NRT;
+        if (wave == r0 / 64) {
+            const int base = r0 % 64;
+            const int mrow = lane - base;
+#pragma unroll
+            for (int cc = BS - CK; cc >= 0; cc -= CK) {
+                T lrow[CK];   // (L^T)_{mrow,c} = l_{c,mrow}, strictly above the diagonal
+#pragma unroll
+                for (int e = 0; e < CK; ++e) {
+                    const int c = cc + e;
+                    lrow[e] = (mrow >= 0 && mrow < c && c < w) ? op_entry<CONJ>(col[r0 + c]) : O::zero();
+                }
+#pragma unroll
+                for (int e = CK - 1; e >= 0; --e) {
+                    const int c = cc + e;
+                    if (c >= w) continue;
+                    T xc[NRT];
+#pragma unroll
+                    for (int r = 0; r < NRT; ++r) xc[r] = readlane_t(y[r], base + c);
+                    if (mrow >= 0 && mrow < c)
+#pragma unroll
+                        for (int r = 0; r < NRT; ++r) O::fms(y[r], lrow[e], xc[r]);
+                }
+            }
+            if (mrow >= 0 && mrow < w)
+#pragma unroll
+                for (int r = 0; r < NRT; ++r) yb[mrow * NRT + r] = y[r];
+        }
+        __syncthreads();
+        if (have && row < r0) {
+#pragma unroll
+            for (int cc = BS - CK; cc >= 0; cc -= CK) {
+                T lrow[CK];
+#pragma unroll
+                for (int e = 0; e < CK; ++e)
+                    lrow[e] = cc + e < w ? op_entry<CONJ>(col[r0 + cc + e]) : O::zero();
+#pragma unroll
+                for (int e = CK - 1; e >= 0; --e) {
+                    if (cc + e >= w) continue;
+#pragma unroll
+                    for (int r = 0; r < NRT; ++r) O::fms(y[r], lrow[e], yb[(cc + e) * NRT + r]);
+                }
+            }
+        }
+    }
+    if (have)
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
+            if (c0 + r < p.nrhs) B[dst + (long long)(c0 + r) * p.ldb] = y[r];
+}
+
 template <typename T, int NRT>
 hipError_t launch_t(const Problem& p, hipStream_t s) {
     const int threads = ((p.n + 63) / 64) * 64;
     const int rt = (p.nrhs + NRT - 1) / NRT;
     const size_t smem = ((p.n * 4 + 15) / 16) * 16 + 2 * BS * NRT * sizeof(T);
-    hipLaunchKernelGGL((getrs_rows_kernel<T, NRT>), dim3((unsigned)((long long)p.batch * rt)), dim3(threads), smem, s,
-                       p, rt);
+    const dim3 grid((unsigned)((long long)p.batch * rt));
+    if (p.trans == 0) {
+        hipLaunchKernelGGL((getrs_rows_kernel<T, NRT>), grid, dim3(threads), smem, s, p, rt);
+    } else if constexpr (ops<T>::is_complex) {
+        if (p.trans == 2)
+            hipLaunchKernelGGL((getrs_rows_trans_kernel<T, NRT, true>), grid, dim3(threads), smem, s, p, rt);
+        else
+            hipLaunchKernelGGL((getrs_rows_trans_kernel<T, NRT, false>), grid, dim3(threads), smem, s, p, rt);
+    } else {   // A^H = A^T for real data
+        hipLaunchKernelGGL((getrs_rows_trans_kernel<T, NRT, false>), grid, dim3(threads), smem, s, p, rt);
+    }
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ struct Problem {
     int* ipiv = nullptr;  long long sP = 0;
     int* info = nullptr;
     void* B = nullptr;  int ldb = 0;  long long sB = 0;
+    int trans = 0;      // getrs: 0 solves A X = B, 1 A^T X = B, 2 A^H X = B
 };
 
 enum Mode { MODE_GETRF = 0, MODE_GESV = 1 };
@@ -28,8 +29,8 @@ hipError_t register_launch(int dtype, const Problem& p, int mode, bool one_wave_
                            hipStream_t s);
 
 // Solve with given factors in one launch (one work-group per matrix and RHS
-// tile, one row per thread), n <= 1024.  With p.info set, matrices whose
-// info is non-zero are skipped (composed gesv).
+// tile, one row per thread), n <= 1024, for every p.trans.  With p.info
+// set, matrices whose info is non-zero are skipped (composed gesv, NoTrans).
 bool getrs_rows_supported(int dtype, int n);
 hipError_t getrs_rows_launch(int dtype, const Problem& p, hipStream_t s);
 

@@ -50,7 +50,7 @@ typedef enum {
 
 /* status codes (negative values -1 .. -20 name an invalid argument) */
 #define BATCHLU_OK 0
-#define BATCHLU_ERR_UNSUPPORTED (-100) /* e.g. trans other than 'N'            */
+#define BATCHLU_ERR_UNSUPPORTED (-100) /* e.g. getrs 'T'/'C' with n > 1024     */
 #define BATCHLU_ERR_CAPACITY (-101)    /* no tier can run this shape           */
 #define BATCHLU_ERR_LAUNCH (-102)      /* a kernel launch failed (HIP error)   */
 
@@ -82,7 +82,8 @@ int batchlu_getrf(batchlu_dtype t, int n, void* A, int lda, long long strideA,
 
 /*
  * batchlu_getrs -- solve op(A) X = B with the factors and ipiv of batchlu_getrf.
- *   1 t, 2 trans ('N' only; 'T'/'C' return BATCHLU_ERR_UNSUPPORTED),
+ *   1 t, 2 trans: 'N' solves A X = B, 'T' A^T X = B, 'C' A^H X = B (A^T
+ *     for real types); 'T'/'C' need n <= 1024, else BATCHLU_ERR_UNSUPPORTED,
  *   3 n, 4 nrhs >= 0, 5 A (device, read only), 6 lda, 7 strideA,
  *   8 ipiv (device, read only; an entry outside 1..n is read as "no
  *     interchange" so that a corrupt list cannot address rows outside B),
@@ -91,7 +92,10 @@ int batchlu_getrf(batchlu_dtype t, int n, void* A, int lda, long long strideA,
  *  12 strideB >= ldb*nrhs when batch > 1, 13 batch, 14 stream.
  * The factors of a matrix whose info was > 0 give inf/NaN, as in LAPACK.
  * Follows: BatchLAS "LU" page, getrs paragraphs (permutation, then forward
- * substitution with unit-lower L, then back substitution with U).
+ * substitution with unit-lower L, then back substitution with U; the fused
+ * kernels exist for NoTrans and Trans).  For op(A) = A^T = U^T L^T P the
+ * order is forward with U^T (division by u_kk), back with unit L^T, then
+ * the interchanges undone in reverse; A^H uses the conjugated factors.
  */
 int batchlu_getrs(batchlu_dtype t, char trans, int n, int nrhs, const void* A,
                   int lda, long long strideA, const int* ipiv,

@@ -59,7 +59,9 @@ def test_getrf_argument_checks(args, expect):
     ((0, "X", 4, 1, FAKE, 4, 16, FAKE, 4, FAKE, 4, 4, 1), -2),    # bad trans
     ((0, "N", 4, -1, FAKE, 4, 16, FAKE, 4, FAKE, 4, 4, 1), -4),   # nrhs < 0
     ((0, "N", 4, 2, FAKE, 4, 16, FAKE, 4, FAKE, 4, 7, 2), -12),   # strideB < ldb*nrhs
-    ((0, "T", 4, 1, FAKE, 4, 16, FAKE, 4, FAKE, 4, 4, 1), -100),  # trans 'T' not built yet
+    ((0, "T", 2000, 1, FAKE, 2000, 4000000, FAKE, 2000, FAKE, 2000, 2000, 1), -100),  # 'T' above n = 1024
+    ((3, "C", 1025, 2, FAKE, 1025, 1050625, FAKE, 1025, FAKE, 1025, 2050, 1), -100),  # 'C' above n = 1024
+    ((0, "T", 0, 1, None, 1, 0, None, 0, None, 1, 1, 3), 0),      # 'T' with n == 0: no work
     ((0, "N", 4, 0, None, 4, 16, None, 4, None, 4, 0, 3), 0),     # nrhs == 0
 ])
 def test_getrs_argument_checks(args, expect):
