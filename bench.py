@@ -273,6 +273,29 @@ def main():
             torch.cuda.synchronize()
             getrf_ms.append(g0.elapsed_time(g1))
         gms = float(np.mean(getrf_ms))
+        # the solve on the factors just made, NoTrans and Trans, each timed on
+        # its own (fresh B, HIP events on the launch stream); algorithmic
+        # bytes: the factors read once, B read and X written
+        es = np.dtype(w.dtype).itemsize
+        solve_bytes = es * (w.n * w.n + 2 * w.n * w.nrhs) * w.batch + 4 * w.n * w.batch
+        solve = {"algorithmic_bytes_per_launch": solve_bytes}
+        dA = sets[(args.steps - 1) % nsets][0]
+        for tr in ("N", "T"):
+            sms = []
+            for i in range(args.steps):
+                dB = sets[i % nsets][1]
+                dB.copy_(hB)
+                torch.cuda.synchronize()
+                s0 = torch.cuda.Event(enable_timing=True)
+                s1 = torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                lib.batchlu_getrs(t, tr, w.n, w.nrhs, dA, w.n, w.n * w.n, ipiv, w.n, dB, w.n, w.n * w.nrhs,
+                                  w.batch, stream=stream)
+                s1.record(stream)
+                torch.cuda.synchronize()
+                sms.append(s0.elapsed_time(s1))
+            ms = float(np.mean(sms))
+            solve[tr] = {"ms": ms, "GB/s": solve_bytes / (ms * 1e-3) / 1e9}
         getrf_flops = 2.0 / 3.0 * w.n ** 3 * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0) * w.batch
         tf = getrf_flops / (gms * 1e-3) / 1e12
         fused = lib.batchlu_select_tier(t, 0, w.n, 0, w.batch) == lib.TIER_BLOCKED and w.n <= 256 and \
@@ -282,7 +305,8 @@ def main():
                 "kernel_ms": gms, "algorithmic_flops_per_launch": getrf_flops,
                 "scope": ("batchlu_getrf = one lu_fused_kernel launch" if fused else
                           "batchlu_getrf = its panel, U12-solve, update and interchange launches"),
-                "whole_step": {"ms": kernel_ms, "tflops": flops_launch / (kernel_ms * 1e-3) / 1e12}}
+                "whole_step": {"ms": kernel_ms, "tflops": flops_launch / (kernel_ms * 1e-3) / 1e12},
+                "getrs": solve}
     line = {
         "metric": METRIC,
         "value": mats_per_s,
