@@ -191,6 +191,25 @@ __device__ inline T op_entry(const T& v) {
     else return v;
 }
 
+// CK consecutive entries of one stored column, op_entry applied, read as
+// 16-byte vectors (src 16-byte aligned): a quarter of the load instructions
+// of element loads for float, which matters because the lanes of a
+// wavefront each read a different column.
+template <bool CONJ, typename T>
+__device__ inline void load_column_run(T (&dst)[CK], const T* src) {
+    constexpr int PER = 16 / (int)sizeof(T);
+    static_assert(CK % PER == 0, "run length");
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+    for (int q = 0; q < CK / PER; ++q) {
+        const uint4 v = s4[q];
+        T tmp[PER];
+        __builtin_memcpy(tmp, &v, 16);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) dst[q * PER + i] = op_entry<CONJ>(tmp[i]);
+    }
+}
+
 template <typename T, int NRT, bool CONJ>
 __global__ void __launch_bounds__(1024) getrs_rows_trans_kernel(Problem p, int rtiles)
 {
@@ -229,6 +248,8 @@ __global__ void __launch_bounds__(1024) getrs_rows_trans_kernel(Problem p, int r
     for (int r = 0; r < NRT; ++r)
         y[r] = (have && c0 + r < p.nrhs) ? B[row + (long long)(c0 + r) * p.ldb] : O::zero();
     const T* col = LU + (long long)row * p.lda;   // column `row`: row `row` of U^T and L^T
+    // every run col[r0 + cc .. +CK) of a full block starts 16-byte aligned
+    const bool vec = (reinterpret_cast<uintptr_t>(LU) % 16 == 0) && (p.lda % (16 / (int)sizeof(T)) == 0);
 
     const int P = (n + BS - 1) / BS;
     // U^T w = b, blocks ascending
@@ -271,9 +292,13 @@ __global__ void __launch_bounds__(1024) getrs_rows_trans_kernel(Problem p, int r
 #pragma unroll
             for (int cc = 0; cc < BS; cc += CK) {
                 T urow[CK];
+                if (vec && w == BS) {
+                    load_column_run<CONJ>(urow, col + r0 + cc);
+                } else {
 #pragma unroll
-                for (int e = 0; e < CK; ++e)
-                    urow[e] = cc + e < w ? op_entry<CONJ>(col[r0 + cc + e]) : O::zero();
+                    for (int e = 0; e < CK; ++e)
+                        urow[e] = cc + e < w ? op_entry<CONJ>(col[r0 + cc + e]) : O::zero();
+                }
 #pragma unroll
                 for (int e = 0; e < CK; ++e) {
                     if (cc + e >= w) continue;
@@ -321,9 +346,13 @@ __global__ void __launch_bounds__(1024) getrs_rows_trans_kernel(Problem p, int r
 #pragma unroll
             for (int cc = BS - CK; cc >= 0; cc -= CK) {
                 T lrow[CK];
+                if (vec && w == BS) {
+                    load_column_run<CONJ>(lrow, col + r0 + cc);
+                } else {
 #pragma unroll
-                for (int e = 0; e < CK; ++e)
-                    lrow[e] = cc + e < w ? op_entry<CONJ>(col[r0 + cc + e]) : O::zero();
+                    for (int e = 0; e < CK; ++e)
+                        lrow[e] = cc + e < w ? op_entry<CONJ>(col[r0 + cc + e]) : O::zero();
+                }
 #pragma unroll
                 for (int e = CK - 1; e >= 0; --e) {
                     if (cc + e >= w) continue;
