@@ -53,6 +53,8 @@ def _load():
             lib.oracle_getrs_trans_batch.argtypes = [i32, i32, i32, i32, vp, i32, i64, ip, i64, vp, i32, i64,
                                                      i32, i32]
             lib.oracle_getrs_trans_batch.restype = i32
+            lib.oracle_getri_batch.argtypes = [i32, i32, vp, i32, i64, ip, i64, vp, i32, i64, i32, i32]
+            lib.oracle_getri_batch.restype = i32
             lib.oracle_gesv_batch.argtypes = [i32, i32, i32, vp, i32, i64, ip, i64, vp, i32, i64, ip, dp, i32, i32]
             lib.oracle_gesv_batch.restype = i32
             _lib = lib
@@ -109,6 +111,17 @@ def getrs(LU, n, lda, strideA, ipiv, B, nrhs, ldb, strideB, batch, nthreads=0, t
                                           _ptr(B), ldb, strideB, batch, nthreads)
     return _load().oracle_getrs_trans_batch(_code(B), code, n, nrhs, _ptr(LU), lda, strideA, _ptr(ipiv),
                                             ipiv.shape[1], _ptr(B), ldb, strideB, batch, nthreads)
+
+
+def getri(LU, n, lda, strideA, ipiv, C, ldc, strideC, batch, nthreads=0):
+    """C = A^{-1} (out of place) from the oracle's (or any) LU + ipiv."""
+    ipiv = np.ascontiguousarray(ipiv, dtype=np.int32).reshape(batch, -1)
+    if batch > 0 and n > 0:
+        _check_flat(C, (batch - 1) * strideC + (n - 1) * ldc + n, "C")
+        if LU.dtype != C.dtype:
+            raise TypeError("LU and C dtypes differ")
+    return _load().oracle_getri_batch(_code(C), n, _ptr(LU), lda, strideA, _ptr(ipiv), ipiv.shape[1],
+                                      _ptr(C), ldc, strideC, batch, nthreads)
 
 
 def gesv(A, n, lda, strideA, B, nrhs, ldb, strideB, batch, want_margins=False, nthreads=0):

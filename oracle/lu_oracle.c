@@ -38,6 +38,10 @@
  *       then L^T z = w, then x = P^T z (transpositions in reverse order);
  *       A^H uses the conjugates of the factors.  Forward sums run in
  *       ascending k, backward sums in descending k, as in R5.
+ *   R8  getri (inverse from the factors; the pages say only that each
+ *       work-item traces its row back through the interchange list and
+ *       writes straight into the output): C = A^{-1} as the solution of
+ *       A C = I with the NoTrans solve of R5, out of place.
  *
  * Arithmetic is in the working precision of the data type (the pivot choice
  * must be reproduced exactly); margins are reported in double.  Build with
@@ -461,6 +465,28 @@ int oracle_getrs_batch(int t, int n, int nrhs, const void* A, int lda,
     J.sA = strideA; J.ipiv = (int*)ipiv; J.sP = strideP; J.B = (char*)B;
     J.ldb = ldb; J.sB = strideB;
     return run_batch(J, batch, nthreads);
+}
+
+/* getri, out of place: C = A^{-1} from the factors and ipiv, as the
+   solution of A C = I (C set to the identity, then the NoTrans solve,
+   column by column).  R8 of the header. */
+int oracle_getri_batch(int t, int n, const void* A, int lda, long long strideA,
+                       const int* ipiv, long long strideP, void* C, int ldc,
+                       long long strideC, int batch, int nthreads)
+{
+    size_t es = elem_size(t);
+    for (int b = 0; b < batch; ++b) {
+        char* c = (char*)C + (size_t)b * strideC * es;
+        for (int j = 0; j < n; ++j) {
+            memset(c + (size_t)j * ldc * es, 0, (size_t)n * es);
+            if (t == OR_R32) ((float*)c)[j + (size_t)j * ldc] = 1.0f;
+            else if (t == OR_R64) ((double*)c)[j + (size_t)j * ldc] = 1.0;
+            else if (t == OR_C64) ((float*)c)[2 * (j + (size_t)j * ldc)] = 1.0f;
+            else ((double*)c)[2 * (j + (size_t)j * ldc)] = 1.0;
+        }
+    }
+    return oracle_getrs_batch(t, n, n, A, lda, strideA, ipiv, strideP, C, ldc, strideC,
+                              batch, nthreads);
 }
 
 /* trans: 0 solves A X = B, 1 solves A^T X = B, 2 solves A^H X = B */

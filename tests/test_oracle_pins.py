@@ -405,6 +405,40 @@ def test_transposed_solve_against_lapack(dtype, n, nrhs, trans):
         assert err <= 64 * n * oracle.eps_of(dtype) * np.linalg.cond(op)
 
 
+def test_integer_inverse_is_exact():
+    """A unimodular integer matrix (det -1) whose factorisation swaps rows and
+    whose pivots are powers of two (4, 1, 2, 1/8): every intermediate value
+    is dyadic, so getri reproduces the integer inverse exactly in double and
+    a wrong interchange order or a transposed operand fails."""
+    A = np.array([[-2, 1, -4, -1], [2, 1, -3, 3], [1, 1, -2, -1], [4, 0, 3, -1]], np.float64)
+    Ainv = np.round(np.linalg.inv(A))
+    np.testing.assert_array_equal(A @ Ainv, np.eye(4))   # the inverse is integral
+    flatA = _flat_colmajor(A)
+    ipiv, info, _, _ = oracle.getrf(flatA, 4, 4, 16, 1)
+    assert info[0] == 0 and list(ipiv[0]) != [1, 2, 3, 4]
+    C = np.full(6 * 4 + 3, 9.0)
+    oracle.getri(flatA, 4, 4, 16, ipiv, C, 6, 27, 1)
+    np.testing.assert_array_equal(oracle.matrix(C, 0, 4, 4, 6, 27), Ainv)
+    assert np.all(C[[4, 5, 10, 11, 16, 17, 22, 23, 24, 25, 26]] == 9.0)   # pads untouched
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64, np.complex64, np.complex128])
+@pytest.mark.parametrize("n", [1, 6, 37])
+def test_inverse_against_lapack(dtype, n):
+    A_all, _ = lu_inputs.random_problem(4242 + n, dtype, n, 0, 3)
+    fa = A_all.copy()
+    ipiv, info, _, _ = oracle.getrf(fa, n, n, n * n, 3)
+    C = np.zeros(3 * n * n, dtype)
+    oracle.getri(fa, n, n, n * n, ipiv, C, n, n * n, 3)
+    wide = np.complex128 if np.iscomplexobj(A_all) else np.float64
+    for b in range(3):
+        A = oracle.matrix(A_all, b, n, n, n, n * n).astype(wide)
+        ref = np.linalg.inv(A)
+        X = oracle.matrix(C, b, n, n, n, n * n)
+        err = np.max(np.abs(X - ref)) / np.max(np.abs(ref))
+        assert err <= 64 * n * oracle.eps_of(dtype) * np.linalg.cond(A)
+
+
 def test_gesv_leaves_b_for_singular_matrix():
     A = np.array([[1, 2], [2, 4]], np.float32)
     B = np.array([[3.0], [7.0]], np.float32)
