@@ -41,13 +41,15 @@ def load():
     lib.batchlu_getrf.argtypes = [i32, i32, vp, i32, i64, vp, i64, vp, i32, vp]
     lib.batchlu_getrs.argtypes = [i32, ch, i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, i32, vp]
     lib.batchlu_gesv.argtypes = [i32, i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, vp, i32, vp]
+    lib.batchlu_getri.argtypes = [i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, i32, vp]
     lib.batchlu_select_tier.argtypes = [i32, i32, i32, i32, i32]
     lib.batchlu_set_tier.argtypes = [i32]
     lib.batchlu_status_string.argtypes = [i32]
     lib.batchlu_status_string.restype = ctypes.c_char_p
     lib.batchlu_version.argtypes = []
     lib.batchlu_version.restype = ctypes.c_char_p
-    for f in ("batchlu_getrf", "batchlu_getrs", "batchlu_gesv", "batchlu_select_tier", "batchlu_set_tier"):
+    for f in ("batchlu_getrf", "batchlu_getrs", "batchlu_gesv", "batchlu_getri", "batchlu_select_tier",
+              "batchlu_set_tier"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -101,6 +103,13 @@ def batchlu_getrs(t, trans, n, nrhs, A, lda, strideA, ipiv, strideP, B, ldb, str
     st = load().batchlu_getrs(t, tr, n, nrhs, _ptr(A), lda, strideA, _ptr(ipiv), strideP, _ptr(B), ldb, strideB,
                               batch, _stream(stream))
     return _check("batchlu_getrs", st, raise_on_error)
+
+
+def batchlu_getri(t, n, A, lda, strideA, ipiv, strideP, C, ldc, strideC, batch, stream=None,
+                  raise_on_error=True):
+    st = load().batchlu_getri(t, n, _ptr(A), lda, strideA, _ptr(ipiv), strideP, _ptr(C), ldc, strideC, batch,
+                              _stream(stream))
+    return _check("batchlu_getri", st, raise_on_error)
 
 
 def batchlu_gesv(t, n, nrhs, A, lda, strideA, ipiv, strideP, B, ldb, strideB, info, batch, stream=None,

@@ -145,6 +145,36 @@ int batchlu_getrs(batchlu_dtype t, char trans, int n, int nrhs, const void* A, i
     return run_getrs(tier, t, p, stream);
 }
 
+int batchlu_getri(batchlu_dtype t, int n, const void* A, int lda, long long strideA, const int* ipiv,
+                  long long strideP, void* C, int ldc, long long strideC, int batch, hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (n < 0) return -2;
+    if (lda < (n > 1 ? n : 1)) return -4;
+    if (ldc < (n > 1 ? n : 1)) return -9;
+    if (batch < 0) return -11;
+    if (batch > 1 && strideA < (long long)lda * n) return -5;
+    if (batch > 1 && strideP < n) return -7;
+    if (batch > 1 && strideC < (long long)ldc * n) return -10;
+    if (n == 0 || batch == 0) return BATCHLU_OK;
+    if (!A) return -3;
+    if (!ipiv) return -6;
+    if (!C) return -8;
+    {   // out of place: the byte ranges of A and C must not meet
+        const long long es = (t == BATCHLU_C128) ? 16 : (t == BATCHLU_R32) ? 4 : 8;
+        const long long ea = es * ((long long)(batch - 1) * strideA + (long long)(n - 1) * lda + n);
+        const long long ec = es * ((long long)(batch - 1) * strideC + (long long)(n - 1) * ldc + n);
+        const char* a0 = (const char*)A;
+        const char* c0 = (const char*)C;
+        if (c0 < a0 + ea && a0 < c0 + ec) return -8;
+    }
+    if (!getrs_rows_supported(t, n)) return BATCHLU_ERR_UNSUPPORTED;   // n > 1024
+    Problem p;
+    p.n = n; p.nrhs = n; p.batch = batch; p.A = const_cast<void*>(A); p.lda = lda; p.sA = strideA;
+    p.ipiv = const_cast<int*>(ipiv); p.sP = strideP; p.B = C; p.ldb = ldc; p.sB = strideC;
+    p.inverse = true;
+    return status_of(getrs_rows_launch(t, p, stream));
+}
+
 int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda, long long strideA, int* ipiv,
                  long long strideP, void* B, int ldb, long long strideB, int* info, int batch,
                  hipStream_t stream) {

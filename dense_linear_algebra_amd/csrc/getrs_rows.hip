@@ -1,6 +1,7 @@
 // getrs_rows.hip -- the whole LU solve of one matrix and one tile of
 // right-hand sides in a single work-group: one row per thread, n <= 1024,
-// for A X = B and (second kernel, below) A^T X = B and A^H X = B.
+// for A X = B (also A C = I, the inverse of getri) and (second kernel,
+// below) A^T X = B and A^H X = B.
 //
 // BatchLAS "LU" page, fused getrs paragraph (one work-group per matrix does
 // the permutation and both substitutions in one launch) and blocked getrs
@@ -24,7 +25,9 @@ namespace {
 constexpr int BS = 32;   // rows per diagonal block
 constexpr int CK = 16;   // columns of L or U loaded per round
 
-template <typename T, int NRT>
+// IDENT: getri.  B is not read; the right-hand sides are the identity's
+// columns, so row `row` of P*I is e_src (one where the column is src).
+template <typename T, int NRT, bool IDENT>
 __global__ void __launch_bounds__(1024) getrs_rows_kernel(Problem p, int rtiles)
 {
     using O = ops<T>;
@@ -62,8 +65,12 @@ __global__ void __launch_bounds__(1024) getrs_rows_kernel(Problem p, int rtiles)
                 src = (src == k) ? pk : (src == pk ? k : src);
             }
 #pragma unroll
-        for (int r = 0; r < NRT; ++r)
-            y[r] = (have && c0 + r < p.nrhs) ? B[src + (long long)(c0 + r) * p.ldb] : O::zero();
+        for (int r = 0; r < NRT; ++r) {
+            if constexpr (IDENT)
+                y[r] = (have && c0 + r < p.nrhs && src == c0 + r) ? O::one() : O::zero();
+            else
+                y[r] = (have && c0 + r < p.nrhs) ? B[src + (long long)(c0 + r) * p.ldb] : O::zero();
+        }
     }
 
     const int P = (n + BS - 1) / BS;
@@ -374,8 +381,10 @@ hipError_t launch_t(const Problem& p, hipStream_t s) {
     const int rt = (p.nrhs + NRT - 1) / NRT;
     const size_t smem = ((p.n * 4 + 15) / 16) * 16 + 2 * BS * NRT * sizeof(T);
     const dim3 grid((unsigned)((long long)p.batch * rt));
-    if (p.trans == 0) {
-        hipLaunchKernelGGL((getrs_rows_kernel<T, NRT>), grid, dim3(threads), smem, s, p, rt);
+    if (p.inverse) {
+        hipLaunchKernelGGL((getrs_rows_kernel<T, NRT, true>), grid, dim3(threads), smem, s, p, rt);
+    } else if (p.trans == 0) {
+        hipLaunchKernelGGL((getrs_rows_kernel<T, NRT, false>), grid, dim3(threads), smem, s, p, rt);
     } else if constexpr (ops<T>::is_complex) {
         if (p.trans == 2)
             hipLaunchKernelGGL((getrs_rows_trans_kernel<T, NRT, true>), grid, dim3(threads), smem, s, p, rt);

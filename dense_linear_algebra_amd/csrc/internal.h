@@ -18,6 +18,7 @@ struct Problem {
     int* info = nullptr;
     void* B = nullptr;  int ldb = 0;  long long sB = 0;
     int trans = 0;      // getrs: 0 solves A X = B, 1 A^T X = B, 2 A^H X = B
+    bool inverse = false;   // getri: B is the output C; the solve runs on the identity
 };
 
 enum Mode { MODE_GETRF = 0, MODE_GESV = 1 };

@@ -116,6 +116,30 @@ int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda,
                  hipStream_t stream);
 
 /*
+ * batchlu_getri -- C = A^{-1} from the factors and ipiv of batchlu_getrf,
+ * out of place.
+ *   1 t, 2 n (0 <= n <= 1024; larger n returns BATCHLU_ERR_UNSUPPORTED),
+ *   3 A (device, read only: the factors), 4 lda >= max(1, n),
+ *   5 strideA >= lda*n when batch > 1,
+ *   6 ipiv (device, read only; an entry outside 1..n is read as "no
+ *     interchange"), 7 strideP >= n when batch > 1,
+ *   8 C (device, out: the n x n inverses; its bytes must not overlap A's,
+ *     else -8), 9 ldc >= max(1, n), 10 strideC >= ldc*n when batch > 1,
+ *  11 batch, 12 stream.
+ * Rows n..ldc-1 of C are not written.  A matrix whose info was > 0 gets
+ * inf/NaN entries (LAPACK returns info there and leaves the inverse
+ * undefined).  Follows: BatchLAS "LU" page, getri paragraph (each row is
+ * traced back through the interchange list in registers and the result is
+ * written straight into C, so no permutation pass is needed): computed as
+ * the NoTrans solve of A C = I, whose right-hand sides never exist in
+ * memory.
+ */
+int batchlu_getri(batchlu_dtype t, int n, const void* A, int lda,
+                  long long strideA, const int* ipiv, long long strideP,
+                  void* C, int ldc, long long strideC, int batch,
+                  hipStream_t stream);
+
+/*
  * batchlu_select_tier -- the tier an AUTO call would use for this shape
  * (op: 0 getrf, 1 getrs, 2 gesv), or BATCHLU_ERR_CAPACITY / -k on bad
  * arguments.  Host only, launches nothing.  Follows: BatchLAS "LU" page,

@@ -25,7 +25,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     so = ctypes.CDLL(_binding.LIB_PATH)
     names = _declared()
-    assert {"batchlu_getrf", "batchlu_getrs", "batchlu_gesv"} <= set(names)
+    assert {"batchlu_getrf", "batchlu_getrs", "batchlu_gesv", "batchlu_getri"} <= set(names)
     for name in names:
         assert hasattr(so, name), f"{name} declared in batchlu.h but not exported"
 
@@ -66,6 +66,21 @@ def test_getrf_argument_checks(args, expect):
 ])
 def test_getrs_argument_checks(args, expect):
     assert lib.batchlu_getrs(*args, stream=0, raise_on_error=False) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, -1, FAKE, 4, 16, FAKE, 4, FAKE, 4, 16, 1), -2),          # n < 0
+    ((0, 4, FAKE, 3, 16, FAKE, 4, FAKE, 4, 16, 1), -4),           # lda < n
+    ((0, 4, FAKE, 4, 16, FAKE, 4, FAKE, 3, 16, 1), -9),           # ldc < n
+    ((0, 4, FAKE, 4, 16, FAKE, 4, FAKE, 4, 15, 2), -10),          # strideC < ldc*n
+    ((0, 4, FAKE, 4, 16, None, 4, FAKE + 4096, 4, 16, 1), -6),    # ipiv null
+    ((0, 4, FAKE, 4, 16, FAKE, 4, FAKE + 60, 4, 16, 1), -8),      # C overlaps A's last element
+    ((0, 4, FAKE, 4, 16, FAKE, 4, FAKE, 4, 16, -1), -11),         # batch < 0
+    ((0, 1100, FAKE, 1100, 1210000, FAKE, 1100, 1 << 40, 1100, 1210000, 1), -100),  # n > 1024
+    ((0, 0, None, 1, 0, None, 0, None, 1, 0, 5), 0),              # n == 0: no work
+])
+def test_getri_argument_checks(args, expect):
+    assert lib.batchlu_getri(*args, stream=0, raise_on_error=False) == expect
 
 
 @pytest.mark.parametrize("args,expect", [
