@@ -296,6 +296,24 @@ def main():
                 sms.append(s0.elapsed_time(s1))
             ms = float(np.mean(sms))
             solve[tr] = {"ms": ms, "GB/s": solve_bytes / (ms * 1e-3) / 1e9}
+        # getri on the same factors: algorithmic bytes = factors read once,
+        # the n x n inverse written
+        dC = torch.empty(w.batch * w.n * w.n, dtype=dA.dtype, device=dev)
+        inv_bytes = 2 * es * w.n * w.n * w.batch + 4 * w.n * w.batch
+        ims = []
+        for i in range(args.steps):
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            lib.batchlu_getri(t, w.n, dA, w.n, w.n * w.n, ipiv, w.n, dC, w.n, w.n * w.n, w.batch, stream=stream)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            ims.append(s0.elapsed_time(s1))
+        ms = float(np.mean(ims))
+        getri = {"ms": ms, "algorithmic_bytes_per_launch": inv_bytes, "GB/s": inv_bytes / (ms * 1e-3) / 1e9,
+                 "TFLOP/s": 4.0 / 3.0 * w.n ** 3 * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0) * w.batch
+                 / (ms * 1e-3) / 1e12}
+        del dC
         getrf_flops = 2.0 / 3.0 * w.n ** 3 * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0) * w.batch
         tf = getrf_flops / (gms * 1e-3) / 1e12
         fused = lib.batchlu_select_tier(t, 0, w.n, 0, w.batch) == lib.TIER_BLOCKED and w.n <= 256 and \
@@ -306,7 +324,7 @@ def main():
                 "scope": ("batchlu_getrf = one lu_fused_kernel launch" if fused else
                           "batchlu_getrf = its panel, U12-solve, update and interchange launches"),
                 "whole_step": {"ms": kernel_ms, "tflops": flops_launch / (kernel_ms * 1e-3) / 1e12},
-                "getrs": solve}
+                "getrs": solve, "getri": getri}
     line = {
         "metric": METRIC,
         "value": mats_per_s,
