@@ -408,6 +408,17 @@ hipError_t getrs_rows_launch(int dtype, const Problem& p, hipStream_t s) {
     // right-hand sides per work-group (each group streams all of L and U;
     // wider tiles were measured slower at n = 1024, nrhs = 32: fewer groups)
     const int r = p.nrhs;
+    if (p.inverse) {
+        // getri has n columns, so wide tiles still leave many work-groups;
+        // each tile streams the factors once, so wider is fewer passes
+        switch (dtype) {
+        case R32: return r <= 4 ? launch_t<float, 4>(p, s) : launch_t<float, 16>(p, s);
+        case R64: return r <= 4 ? launch_t<double, 4>(p, s) : launch_t<double, 8>(p, s);
+        case C64: return r <= 4 ? launch_t<cplx<float>, 4>(p, s) : launch_t<cplx<float>, 8>(p, s);
+        case C128: return launch_t<cplx<double>, 4>(p, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (dtype) {
     case R32: return r <= 1 ? launch_t<float, 1>(p, s) : launch_t<float, 4>(p, s);
     case R64: return r <= 1 ? launch_t<double, 1>(p, s) : launch_t<double, 4>(p, s);
