@@ -103,3 +103,37 @@ def relayout(flat: np.ndarray, rows: int, cols: int, batch: int, ld_in: int, str
             dst = b * stride_out + j * ld_out
             out[dst: dst + rows] = flat[src: src + rows]
     return out[:total] if total > 0 else out[:0]
+
+
+def zero_pivot_problem(seed: int, dtype, n: int, nrhs: int, batch: int):
+    """Matrices with exactly-zero pivots whose pivot rows carry an infinity
+    and signed zeros into the trailing columns.
+
+    Matrix b: iid uniform[-1, 1] entries (complex: both parts), a leading
+    diagonal of 64 (so that no rows move before the first zero pivot), one or
+    two columns that are entirely +-0 (so that their pivot is exactly zero
+    whatever happens before), +inf in the trailing part of the first zero
+    pivot's row, and a column of -0 below a 1 in that row.  Used to check
+    that a step with a zero pivot changes nothing beyond its own column (no
+    0 * inf, no +0 replacing a -0)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    mats = []
+    for b in range(batch):
+        M = draw(rng, dtype, n * n).reshape(n, n)   # row-major view of the draw
+        z = [5 + (b % 3)] + ([37 + (b % 5)] if n > 48 else [])
+        for j in range(z[0]):
+            M[j, j] = 64
+        for zc in z:
+            col = np.zeros(n, dtype)
+            col[1::2] = -0.0
+            M[:, zc] = col
+        zr = z[0]
+        if n > 40:
+            cinf, cneg = n - 3, n - 7
+            M[zr, cinf] = np.inf
+            M[:, cneg] = -0.0
+            M[zr, cneg] = 1
+        mats.append(np.ascontiguousarray(M.T).reshape(-1))    # column-major
+    A = np.concatenate(mats) if mats else np.zeros(0, dtype)
+    B = draw(rng, dtype, batch * n * nrhs)
+    return A, B

@@ -23,6 +23,10 @@ def _num(v):
     if isinstance(v, list):
         return complex(_num(v[0]), _num(v[1]))
     if isinstance(v, str):
+        if v.startswith("f32:0x"):
+            return float(np.array([int(v[4:], 16)], np.uint32).view(np.float32)[0])
+        if v.startswith("f64:0x"):
+            return float(np.array([int(v[4:], 16)], np.uint64).view(np.float64)[0])
         if "*2^" in v:
             m, e = v.split("*2^")
             return math.ldexp(float(m), int(e))
@@ -45,6 +49,11 @@ def _factor_one(M):
     return oracle.matrix(flat, 0, n, n, n, n * n), ipiv[0], int(info[0]), margins[0]
 
 
+def _bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view({4: np.uint32, 8: np.uint64, 16: np.uint64}[a.dtype.itemsize])
+
+
 def _cases():
     with open(GOLDEN) as f:
         data = json.load(f)
@@ -61,15 +70,16 @@ def test_hand_worked(case, dtype):
     assert info == case["info"]
     if case["LU"] is not None:
         want = _mat(case["LU"], dtype)
-        np.testing.assert_array_equal(LU, want)
+        # bit for bit: -0 differs from +0, and a last-bit difference fails
+        assert np.array_equal(_bits(LU), _bits(want)), f"LU {LU!r} != {want!r}"
     if "B" in case:
         n = A.shape[0]
         B = _mat(case["B"], dtype)
         flatA = _flat_colmajor(A)
         flatB = _flat_colmajor(B)
         ipiv2, info2, _, _ = oracle.gesv(flatA, n, n, n * n, flatB, B.shape[1], n, n * B.shape[1], 1)
-        np.testing.assert_array_equal(oracle.matrix(flatB, 0, n, B.shape[1], n, n * B.shape[1]),
-                                      _mat(case["X"], dtype))
+        X = oracle.matrix(flatB, 0, n, B.shape[1], n, n * B.shape[1])
+        assert np.array_equal(_bits(X), _bits(_mat(case["X"], dtype))), f"X {X!r}"
 
 
 # ---------------------------------------------------------------- closed forms
