@@ -1,12 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the batched gesv hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
 
-A step is one batched gesv call (factor + forward + back substitution for
-every matrix of the batch) on synthetic inputs already resident in HBM.  The
-factorisation is in place, so every step gets its own pre-copied input set
-(copies happen before the timed region).  Prints one JSON line.
+A step is one batched gesv (factor + forward + back substitution of every
+matrix of the batch; for the n = 1024 workload getrf then getrs) on synthetic
+inputs already resident in HBM.  The factorisation is in place, so every step
+runs on its own pre-copied input set, and the sets rotate through enough
+bytes that they cannot all sit in the 256 MB last-level cache; copies happen
+outside the timed regions.
+
+One JSON line.  The headline (``value``) is sgesv n = 32, nrhs = 8,
+batch 32768: K steps bracketed by a synchronisation on both sides, wall
+clock.  ``workloads`` carries every workload of the metric, each with the
+median per-step time over at least 7 event-timed steps, the back-to-back
+rate, the roofline of its dominant kernel and the oracle's host rate on all
+cores and on one core.
 """
 from __future__ import annotations
 
@@ -25,10 +34,14 @@ sys.path.insert(0, ROOT)
 import lu_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-FP32_ALU_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop x 2.4 GHz, no packed FP32
 FP32_MFMA_PEAK_TFLOPS = 157.3
 FP64_PEAK_TFLOPS = 78.6
 METRIC = "batched gesv matrices/s + GFLOP/s (n=32 f32, n=256 f64), % of roofline"
+HEADLINE = "sgesv_n32_r8_b32768"
+ORDER = ["sgesv_n16_b1024", "sgesv_n32_r8_b32768", "cgesv_n64_r16_b8192", "dgesv_n256_b1024",
+         "sgetrf_sgetrs_n1024_r32_b64"]
+ROTATE_BYTES = 320 << 20          # in-place input bytes the rotating sets span at least
+MAX_SETS = 600
 # sources of the kernel whose HBM counters a workload's summary records
 # (the summary is used only while these sources are unchanged)
 _C = "dense_linear_algebra_amd/csrc/"
@@ -37,6 +50,7 @@ KERNEL_SOURCES = {
     "sgesv_n32_r8_b32768": [_C + "register_lu_row16.h", _C + "device_ops.h"],
     "cgesv_n64_r16_b8192": [_C + "register_lu_kernel.h", _C + "device_ops.h"],
     "dgesv_n256_b1024": [_C + "blocked_fused.hip", _C + "device_ops.h"],
+    "sgetrf_sgetrs_n1024_r32_b64": [_C + "blocked_lu.hip", _C + "device_ops.h"],
 }
 
 
@@ -52,6 +66,10 @@ def algorithmic_flops(w) -> float:
     return f * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0)
 
 
+def getrf_flops(w) -> float:
+    return 2.0 / 3.0 * w.n ** 3 * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0)
+
+
 def source_hash(workload: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES.get(workload, []):
@@ -64,10 +82,8 @@ def traffic_from_profile(workload: str):
     """HBM bytes per launch of the workload's dominant kernel from the
     committed rocprofv3 counter summary, if it was taken on the current kernel
     source; else None."""
-    if workload not in KERNEL_SOURCES:
-        return None
     path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
-    if not os.path.exists(path):
+    if workload not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     try:
         with open(path) as f:
@@ -80,7 +96,7 @@ def traffic_from_profile(workload: str):
 
 
 def _counter_rows(db: str):
-    """(kernel name, dispatch id, counter value) rows of one rocprofv3 --pmc
+    """(kernel name, counter value) per dispatch of one rocprofv3 --pmc
     database, read through rocpd2csv."""
     import csv
     import subprocess
@@ -100,7 +116,9 @@ def _counter_rows(db: str):
 def write_counter_summary(workload: str, kernel: str, fetch_db: str, write_db: str, copy_mb: int, commands):
     """HBM bytes per launch of `kernel` from a FETCH_SIZE and a WRITE_SIZE run,
     each scaled by what the counter reads for the plain device copy of
-    copy_mb MiB that the same run made first (bench.py --copy-probe-mb)."""
+    copy_mb MiB that the same run made first (bench.py --copy-probe-mb).
+    For a workload whose step is several launches, `kernel` is the dominant
+    one and the bytes are per launch of it."""
     w = lu_inputs.WORKLOADS[workload]
     res = {"kernel": kernel, "workload": workload, "source_hash": source_hash(workload), "commands": list(commands)}
     per = {}
@@ -129,20 +147,210 @@ def write_counter_summary(workload: str, kernel: str, fetch_db: str, write_db: s
     print(path)
 
 
-def cpu_baseline(w, A, B, budget_s: float = 10.0):
-    """The oracle (as is) on host cores: whole-batch gesv repeated until about
-    budget_s of wall time has elapsed."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on host cores
+# ---------------------------------------------------------------------------
+
+def _oracle_step(w, A, B, m, nthreads):
     import oracle
-    reps, used, t_total, mats = 0, 0, 0.0, 0
-    while t_total < budget_s and reps < 1000:
-        a, b = A.copy(), B.copy()
+    n, r = w.n, w.nrhs
+    a = A[: m * n * n].copy()
+    b = B[: m * n * r].copy()
+    t0 = time.perf_counter()
+    if w.op == "gesv":
+        _, _, _, used = oracle.gesv(a, n, n, n * n, b, r, n, n * r, m, nthreads=nthreads)
+    else:
+        ipiv, _, _, used = oracle.getrf(a, n, n, n * n, m, nthreads=nthreads)
+        oracle.getrs(a, n, n, n * n, ipiv, b, r, n, n * r, m, nthreads=nthreads)
+    return time.perf_counter() - t0, int(used)
+
+
+def _oracle_rate(w, A, B, nthreads, min_run_s):
+    """Matrices/s of the oracle on the first m matrices (m doubled until one
+    run takes min_run_s or the batch is used up), median of 3 runs."""
+    m = 1 if nthreads == 1 else min(w.batch, os.cpu_count() or 1)
+    while True:
+        dt, used = _oracle_step(w, A, B, m, nthreads)
+        if dt >= min_run_s or m >= w.batch:
+            break
+        m = min(w.batch, m * 2)
+    times = sorted([dt] + [_oracle_step(w, A, B, m, nthreads)[0] for _ in range(2)])
+    return m / times[1], used, m, times[1]
+
+
+def cpu_baseline(w, A, B, min_run_s):
+    all_rate, used, m_all, t_all = _oracle_rate(w, A, B, 0, min_run_s)
+    one_rate, _, m_one, t_one = _oracle_rate(w, A, B, 1, min_run_s)
+    return {"value": all_rate, "unit": "matrices/s", "cores": used, "kind": "oracle",
+            "sample": f"median of 3 runs of the oracle's {w.op} on the first {m_all} matrices of the batch "
+                      f"({t_all:.2f} s each, {used} threads)",
+            "single_core": {"value": one_rate, "unit": "matrices/s", "cores": 1,
+                            "sample": f"median of 3 runs on the first {m_one} matrices ({t_one:.2f} s each)"}}
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+class Runner:
+    """Input sets of one workload on the device and the calls that time them."""
+
+    def __init__(self, lib, torch, w, nsets):
+        self.lib, self.torch, self.w = lib, torch, w
+        dev = torch.device("cuda:0")
+        A, B = lu_inputs.dense_problem(w)
+        self.hA, self.hB = A, B
+        self.pA = torch.from_numpy(A).to(dev)
+        self.pB = torch.from_numpy(B).to(dev)
+        self.sets = [(self.pA.clone(), self.pB.clone()) for _ in range(nsets)]
+        self.ipiv = torch.empty(w.batch * w.n, dtype=torch.int32, device=dev)
+        self.info = torch.empty(w.batch, dtype=torch.int32, device=dev)
+        self.t = lib.dtype_code(A.dtype)
+        self.stream = torch.cuda.current_stream()
+        self.dev = dev
+
+    def restore(self, k=None):
+        for dA, dB in self.sets[: k]:
+            dA.copy_(self.pA)
+            dB.copy_(self.pB)
+        self.torch.cuda.synchronize()
+
+    def step(self, i):
+        w, lib, t = self.w, self.lib, self.t
+        dA, dB = self.sets[i % len(self.sets)]
+        n, r = w.n, w.nrhs
+        if w.op == "gesv":
+            lib.batchlu_gesv(t, n, r, dA, n, n * n, self.ipiv, n, dB, n, n * r, self.info, w.batch,
+                             stream=self.stream)
+        else:
+            lib.batchlu_getrf(t, n, dA, n, n * n, self.ipiv, n, self.info, w.batch, stream=self.stream)
+            lib.batchlu_getrs(t, "N", n, r, dA, n, n * n, self.ipiv, n, dB, n, n * r, w.batch, stream=self.stream)
+
+    def timed_each(self, fn, reps):
+        """HIP events around each of `reps` calls of fn(i) on the launch
+        stream; per-call milliseconds."""
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i, (e0, e1) in enumerate(evs):
+            e0.record(self.stream)
+            fn(i)
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    def back_to_back(self, first, k):
+        """k steps on sets first .. first+k-1 between two synchronisations:
+        (wall ms per step, event ms per step)."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        _, _, _, used = oracle.gesv(a, w.n, w.n, w.n * w.n, b, w.nrhs, w.n, w.n * w.nrhs, w.batch)
-        t_total += time.perf_counter() - t0
-        reps += 1
-        mats += w.batch
-    return {"value": mats / t_total, "unit": "matrices/s", "cores": int(used), "kind": "oracle",
-            "sample": f"{reps} x the full batch of {w.batch} ({t_total:.1f} s wall)"}
+        e0.record(self.stream)
+        for i in range(first, first + k):
+            self.step(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall * 1e3 / k, e0.elapsed_time(e1) / k
+
+    def free(self):
+        del self.sets, self.pA, self.pB
+        self.torch.cuda.empty_cache()
+
+
+def nsets_for(w, k):
+    per = np.dtype(w.dtype).itemsize * w.n * (w.n + w.nrhs) * w.batch
+    return int(min(MAX_SETS, max(k, -(-ROTATE_BYTES // per))))
+
+
+def parity_sample(r, k):
+    """LU of the first k matrices of set 0 (just factorised) against the
+    oracle, bit for bit."""
+    import oracle
+    w = r.w
+    n = w.n
+    a0 = r.hA[: k * n * n].copy()
+    b0 = r.hB[: k * n * w.nrhs].copy()
+    oracle.gesv(a0, n, n, n * n, b0, w.nrhs, n, n * w.nrhs, k)
+    gA0 = r.sets[0][0][: k * n * n].cpu().numpy()
+    return {"sampled_matrices": k, "lu_bitwise_equal": bool(np.array_equal(gA0.view(np.uint8), a0.view(np.uint8)))}
+
+
+def measure(lib, torch, w, steps, warmup, cpu_s, with_cpu):
+    """Every figure of one workload; the dict that goes into the line."""
+    reps = max(7, steps)
+    nsets = nsets_for(w, max(reps, warmup + steps))
+    r = Runner(lib, torch, w, nsets)
+    tier = lib.batchlu_select_tier(r.t, 2 if w.op == "gesv" else 0, w.n, w.nrhs, w.batch)
+    for i in range(warmup):
+        r.step(i)
+    torch.cuda.synchronize()
+    parity = parity_sample(r, 2 if w.n >= 512 else min(16, w.batch)) if warmup > 0 else None
+    r.restore()
+    wall_ms, b2b_ms = r.back_to_back(0, min(steps, nsets))
+    r.restore()
+    each = r.timed_each(r.step, reps)
+    med = float(np.median(each))
+    mean = float(np.mean(each))
+    bytes_launch = algorithmic_bytes(w) * w.batch
+    out = {"n": w.n, "nrhs": w.nrhs, "batch": w.batch, "dtype": np.dtype(w.dtype).name, "op": w.op,
+           "tier": lib.TIER_NAMES.get(tier, str(tier)), "input_sets": nsets,
+           "rotated_bytes": int(np.dtype(w.dtype).itemsize * w.n * (w.n + w.nrhs) * w.batch * nsets),
+           "step_ms_median": med, "step_ms_mean": mean, "step_ms_back_to_back": b2b_ms,
+           "wall_ms_per_step": wall_ms, "reps": reps,
+           "matrices_per_s": w.batch / (med * 1e-3), "matrices_per_s_back_to_back": w.batch / (b2b_ms * 1e-3),
+           "gflops": algorithmic_flops(w) * w.batch / (med * 1e-3) / 1e9, "parity": parity}
+    if tier in (lib.TIER_TINY, lib.TIER_CTA):
+        # one launch per step: the step is the dominant kernel
+        gbs = bytes_launch / (mean * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": gbs / HBM_PEAK_GBS, "traffic": traffic_from_profile(w.name),
+                           "kernel_ms_mean": mean, "kernel_ms_median": med,
+                           "algorithmic_bytes_per_launch": bytes_launch}
+    else:
+        # blocked tier: the factorisation is the dominant part; timed on its
+        # own (fresh copies of the same inputs) against the FP roof
+        peak = FP64_PEAK_TFLOPS if np.dtype(w.dtype) in (np.float64, np.complex128) else FP32_MFMA_PEAK_TFLOPS
+        n = w.n
+        r.restore()
+        g = r.timed_each(lambda i: lib.batchlu_getrf(r.t, n, r.sets[i % nsets][0], n, n * n, r.ipiv, n, r.info,
+                                                     w.batch, stream=r.stream), reps)
+        gmed, gmean = float(np.median(g)), float(np.mean(g))
+        fl = getrf_flops(w) * w.batch
+        tf = fl / (gmean * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
+                           "traffic": traffic_from_profile(w.name), "kernel_ms_mean": gmean,
+                           "kernel_ms_median": gmed, "algorithmic_flops_per_launch": fl,
+                           "scope": "batchlu_getrf (every launch it makes)"}
+        if w.op != "gesv":
+            # the solve and the inverse on the factors of the last getrf
+            es = np.dtype(w.dtype).itemsize
+            dA = r.sets[(reps - 1) % nsets][0].clone()   # the factors that r.ipiv belongs to
+            solve_bytes = es * (n * n + 2 * n * w.nrhs) * w.batch + 4 * n * w.batch
+            solve = {"algorithmic_bytes_per_launch": solve_bytes}
+            for tr in ("N", "T"):
+                for _, dB in r.sets:
+                    dB.copy_(r.pB)
+                ms = r.timed_each(lambda i: lib.batchlu_getrs(r.t, tr, n, w.nrhs, dA, n, n * n, r.ipiv, n,
+                                                              r.sets[i % nsets][1], n, n * w.nrhs, w.batch,
+                                                              stream=r.stream), reps)
+                m = float(np.median(ms))
+                solve[tr] = {"ms_median": m, "GB/s": solve_bytes / (m * 1e-3) / 1e9}
+            out["getrs"] = solve
+            dC = torch.empty(w.batch * n * n, dtype=dA.dtype, device=r.dev)
+            inv_bytes = 2 * es * n * n * w.batch + 4 * n * w.batch
+            ms = r.timed_each(lambda i: lib.batchlu_getri(r.t, n, dA, n, n * n, r.ipiv, n, dC, n, n * n, w.batch,
+                                                          stream=r.stream), max(3, min(reps, 7)))
+            m = float(np.median(ms))
+            out["getri"] = {"ms_median": m, "algorithmic_bytes_per_launch": inv_bytes,
+                            "GB/s": inv_bytes / (m * 1e-3) / 1e9,
+                            "TFLOP/s": 4.0 / 3.0 * n ** 3 * w.batch / (m * 1e-3) / 1e12}
+            del dC, dA
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, r.hA, r.hB, cpu_s)
+    r.free()
+    return out
 
 
 def main():
@@ -150,9 +358,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="sgesv_n32_r8_b32768", choices=sorted(lu_inputs.WORKLOADS))
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(lu_inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--cpu-run-s", type=float, default=0.4, help="least wall time of one timed oracle run")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this size first (reference for HBM counters)")
     ap.add_argument("--counters-summary", nargs=3, metavar=("KERNEL", "FETCH_DB", "WRITE_DB"),
@@ -162,7 +370,8 @@ def main():
     if args.counters_summary:
         kern, fdb, wdb = args.counters_summary
         mb = args.copy_probe_mb or 256
-        base = f"python3 bench.py --workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline --copy-probe-mb {mb}"
+        base = (f"python3 bench.py --workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline "
+                f"--copy-probe-mb {mb}")
         write_counter_summary(args.workload, kern, fdb, wdb, mb,
                               [f"rocprofv3 --pmc FETCH_SIZE -d <dir> -o f -- {base}",
                                f"rocprofv3 --pmc WRITE_SIZE -d <dir> -o w -- {base}"])
@@ -181,153 +390,27 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     lib.load()
-    w = lu_inputs.WORKLOADS[args.workload]
-    A, B = lu_inputs.dense_problem(w)
-    dev = torch.device("cuda:0")
-    t = lib.dtype_code(A.dtype)
-    hA = torch.from_numpy(A)
-    hB = torch.from_numpy(B)
-    nsets = args.warmup + args.steps
-    sets = []
-    for _ in range(nsets):
-        sets.append((hA.to(dev), hB.to(dev)))
-    ipiv = torch.empty(w.batch * w.n, dtype=torch.int32, device=dev)
-    info = torch.empty(w.batch, dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
-    tier = lib.batchlu_select_tier(t, 2, w.n, w.nrhs, w.batch)
-
-    def step(i):
-        dA, dB = sets[i]
-        if w.op == "gesv":
-            lib.batchlu_gesv(t, w.n, w.nrhs, dA, w.n, w.n * w.n, ipiv, w.n, dB, w.n, w.n * w.nrhs, info, w.batch,
-                             stream=stream)
-        else:
-            lib.batchlu_getrf(t, w.n, dA, w.n, w.n * w.n, ipiv, w.n, info, w.batch, stream=stream)
-            lib.batchlu_getrs(t, "N", w.n, w.nrhs, dA, w.n, w.n * w.n, ipiv, w.n, dB, w.n, w.n * w.nrhs, w.batch,
-                              stream=stream)
-
     if args.copy_probe_mb > 0:
-        src = torch.empty(args.copy_probe_mb << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        src = torch.empty(args.copy_probe_mb << 18, dtype=torch.float32, device="cuda:0").fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # quick parity sample of the first warm-up output against the oracle
-    parity = None
-    if args.warmup > 0:
-        import oracle
-        k = min(16, w.batch)
-        a0 = A[: k * w.n * w.n].copy()
-        b0 = B[: k * w.n * w.nrhs].copy()
-        oip, oinfo, _, _ = oracle.gesv(a0, w.n, w.n, w.n * w.n, b0, w.nrhs, w.n, w.n * w.nrhs, k,
-                                       nthreads=0)
-        gA0 = sets[0][0][: k * w.n * w.n].cpu().numpy()
-        parity = {"sampled_matrices": k,
-                  "lu_bitwise_equal": bool(np.array_equal(gA0.view(np.uint8), a0.view(np.uint8)))}
-
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.warmup, nsets):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
-
-    ms_per_step = wall * 1e3 / args.steps
-    mats_per_s = w.batch / (ms_per_step * 1e-3)
-    bytes_launch = algorithmic_bytes(w) * w.batch
-    flops_launch = algorithmic_flops(w) * w.batch
-    achieved_gbs = bytes_launch / (kernel_ms * 1e-3) / 1e9
-    gflops = flops_launch / (ms_per_step * 1e-3) / 1e9
-    kind = "register" if tier in (lib.TIER_TINY, lib.TIER_CTA) else "blocked"
-    if kind == "register":
-        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profile(w.name),
-                "kernel_ms": kernel_ms, "algorithmic_bytes_per_launch": bytes_launch}
-    else:
-        # blocked tier: the factorisation is the dominant part of the step;
-        # it is timed on its own (HIP events on the launch stream, fresh
-        # copies of the same inputs) against the FP roof, the whole step
-        # beside it
-        peak = FP64_PEAK_TFLOPS if np.dtype(w.dtype) in (np.float64, np.complex128) else FP32_MFMA_PEAK_TFLOPS
-        getrf_ms = []
-        for i in range(args.steps):
-            dA = sets[i % nsets][0]
-            dA.copy_(hA)
-            torch.cuda.synchronize()
-            g0 = torch.cuda.Event(enable_timing=True)
-            g1 = torch.cuda.Event(enable_timing=True)
-            g0.record(stream)
-            lib.batchlu_getrf(t, w.n, dA, w.n, w.n * w.n, ipiv, w.n, info, w.batch, stream=stream)
-            g1.record(stream)
-            torch.cuda.synchronize()
-            getrf_ms.append(g0.elapsed_time(g1))
-        gms = float(np.mean(getrf_ms))
-        # the solve on the factors just made, NoTrans and Trans, each timed on
-        # its own (fresh B, HIP events on the launch stream); algorithmic
-        # bytes: the factors read once, B read and X written
-        es = np.dtype(w.dtype).itemsize
-        solve_bytes = es * (w.n * w.n + 2 * w.n * w.nrhs) * w.batch + 4 * w.n * w.batch
-        solve = {"algorithmic_bytes_per_launch": solve_bytes}
-        dA = sets[(args.steps - 1) % nsets][0]
-        for tr in ("N", "T"):
-            sms = []
-            for i in range(args.steps):
-                dB = sets[i % nsets][1]
-                dB.copy_(hB)
-                torch.cuda.synchronize()
-                s0 = torch.cuda.Event(enable_timing=True)
-                s1 = torch.cuda.Event(enable_timing=True)
-                s0.record(stream)
-                lib.batchlu_getrs(t, tr, w.n, w.nrhs, dA, w.n, w.n * w.n, ipiv, w.n, dB, w.n, w.n * w.nrhs,
-                                  w.batch, stream=stream)
-                s1.record(stream)
-                torch.cuda.synchronize()
-                sms.append(s0.elapsed_time(s1))
-            ms = float(np.mean(sms))
-            solve[tr] = {"ms": ms, "GB/s": solve_bytes / (ms * 1e-3) / 1e9}
-        # getri on the same factors: algorithmic bytes = factors read once,
-        # the n x n inverse written
-        dC = torch.empty(w.batch * w.n * w.n, dtype=dA.dtype, device=dev)
-        inv_bytes = 2 * es * w.n * w.n * w.batch + 4 * w.n * w.batch
-        ims = []
-        for i in range(args.steps):
-            s0 = torch.cuda.Event(enable_timing=True)
-            s1 = torch.cuda.Event(enable_timing=True)
-            s0.record(stream)
-            lib.batchlu_getri(t, w.n, dA, w.n, w.n * w.n, ipiv, w.n, dC, w.n, w.n * w.n, w.batch, stream=stream)
-            s1.record(stream)
-            torch.cuda.synchronize()
-            ims.append(s0.elapsed_time(s1))
-        ms = float(np.mean(ims))
-        getri = {"ms": ms, "algorithmic_bytes_per_launch": inv_bytes, "GB/s": inv_bytes / (ms * 1e-3) / 1e9,
-                 "TFLOP/s": 4.0 / 3.0 * w.n ** 3 * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0) * w.batch
-                 / (ms * 1e-3) / 1e12}
-        del dC
-        getrf_flops = 2.0 / 3.0 * w.n ** 3 * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0) * w.batch
-        tf = getrf_flops / (gms * 1e-3) / 1e12
-        fused = lib.batchlu_select_tier(t, 0, w.n, 0, w.batch) == lib.TIER_BLOCKED and w.n <= 256 and \
-            np.dtype(w.dtype).kind == "f"
-        roof = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
-                "traffic": traffic_from_profile(w.name) if fused else None,
-                "kernel_ms": gms, "algorithmic_flops_per_launch": getrf_flops,
-                "scope": ("batchlu_getrf = one lu_fused_kernel launch" if fused else
-                          "batchlu_getrf = its panel, U12-solve, update and interchange launches"),
-                "whole_step": {"ms": kernel_ms, "tflops": flops_launch / (kernel_ms * 1e-3) / 1e12},
-                "getrs": solve, "getri": getri}
+    names = ORDER if args.workload == "all" else [args.workload]
+    head = HEADLINE if args.workload == "all" else args.workload
+    results = {}
+    for name in names:
+        print(f"# {name}", file=sys.stderr, flush=True)
+        results[name] = measure(lib, torch, lu_inputs.WORKLOADS[name], args.steps, args.warmup, args.cpu_run_s,
+                                not args.no_cpu_baseline)
+    h = results[head]
+    w = lu_inputs.WORKLOADS[head]
+    ms_per_step = h["wall_ms_per_step"]
     line = {
         "metric": METRIC,
-        "value": mats_per_s,
+        "value": w.batch / (ms_per_step * 1e-3),
         "unit": "matrices/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -336,16 +419,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"float32": "f32", "float64": "f64", "complex64": "c64", "complex128": "c128"}[np.dtype(w.dtype).name],
+        "dtype": {"float32": "f32", "float64": "f64", "complex64": "c64", "complex128": "c128"}[h["dtype"]],
         "data": "synthetic",
-        "config": {"workload": w.name, "op": w.op, "n": w.n, "nrhs": w.nrhs, "batch": w.batch,
-                   "tier": lib.TIER_NAMES.get(tier, str(tier))},
-        "gflops": gflops,
-        "roofline": roof,
-        "parity": parity,
+        "config": {"workload": head, "op": w.op, "n": w.n, "nrhs": w.nrhs, "batch": w.batch, "tier": h["tier"]},
+        "gflops": algorithmic_flops(w) * w.batch / (ms_per_step * 1e-3) / 1e9,
+        "roofline": h["roofline"],
+        "parity": h["parity"],
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, A, B, args.cpu_budget)
+    if "cpu_baseline" in h:
+        line["cpu_baseline"] = h["cpu_baseline"]
+    line["workloads"] = results
     print(json.dumps(line), flush=True)
 
 

@@ -42,6 +42,8 @@ def load():
     lib.batchlu_getrs.argtypes = [i32, ch, i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, i32, vp]
     lib.batchlu_gesv.argtypes = [i32, i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, vp, i32, vp]
     lib.batchlu_getri.argtypes = [i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, i32, vp]
+    lib.batchlu_check_reciprocal.argtypes = [ctypes.c_uint, ctypes.c_uint, vp, vp, vp]
+    lib.batchlu_check_reciprocal.restype = i32
     lib.batchlu_select_tier.argtypes = [i32, i32, i32, i32, i32]
     lib.batchlu_set_tier.argtypes = [i32]
     lib.batchlu_status_string.argtypes = [i32]
@@ -117,6 +119,11 @@ def batchlu_gesv(t, n, nrhs, A, lda, strideA, ipiv, strideP, B, ldb, strideB, in
     st = load().batchlu_gesv(t, n, nrhs, _ptr(A), lda, strideA, _ptr(ipiv), strideP, _ptr(B), ldb, strideB,
                              _ptr(info), batch, _stream(stream))
     return _check("batchlu_gesv", st, raise_on_error)
+
+
+def batchlu_check_reciprocal(lo_bits, hi_bits, mismatches, first_bad, stream=None, raise_on_error=True):
+    st = load().batchlu_check_reciprocal(lo_bits, hi_bits, _ptr(mismatches), _ptr(first_bad), _stream(stream))
+    return _check("batchlu_check_reciprocal", st, raise_on_error)
 
 
 def batchlu_select_tier(t, op, n, nrhs, batch):

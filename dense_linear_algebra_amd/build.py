@@ -1,6 +1,6 @@
 """Build libbatchlu.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m dense_linear_algebra_amd.build [-v]
+    python -m dense_linear_algebra_amd.build [-v] [--incremental] [--resources]
 
 Every HIP source is compiled with IEEE semantics: -ffp-contract=off (no fused
 multiply-add except the ones the code spells), no fast-math, and without the
@@ -34,8 +34,19 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str, verbose: bool, extra=()):
+def _stale(src: str, obj: str) -> bool:
+    """True when obj is missing or older than src or any header it may include."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [src] + glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(INCLUDE, "*.h"))
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def _compile(src: str, verbose: bool, extra=(), incremental=False):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if incremental and not extra and not _stale(src, obj):
+        return obj, ""
     cmd = [HIPCC, "-c", src, "-o", obj] + COMMON + list(extra)
     if src.endswith(".hip"):
         cmd += DEVICE
@@ -51,13 +62,15 @@ def _compile(src: str, verbose: bool, extra=()):
     return obj, r.stderr
 
 
-def build_library(verbose: bool = False, jobs: int | None = None, extra=()) -> str:
-    """Compile every source (in parallel) and link libbatchlu.so; always rebuilds."""
+def build_library(verbose: bool = False, jobs: int | None = None, extra=(), incremental: bool = False) -> str:
+    """Compile every source (in parallel) and link libbatchlu.so.  Rebuilds
+    every object unless ``incremental``, which recompiles only objects older
+    than their source or any header of the package."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = [o for o, _ in ex.map(lambda s: _compile(s, verbose, extra), srcs)]
+        objs = [o for o, _ in ex.map(lambda s: _compile(s, verbose, extra, incremental), srcs)]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     if verbose:
@@ -70,4 +83,4 @@ def build_library(verbose: bool = False, jobs: int | None = None, extra=()) -> s
 if __name__ == "__main__":
     v = "-v" in sys.argv
     extra = ["-Rpass-analysis=kernel-resource-usage"] if "--resources" in sys.argv else []
-    print(build_library(verbose=v, extra=extra))
+    print(build_library(verbose=v, extra=extra, incremental="--incremental" in sys.argv))

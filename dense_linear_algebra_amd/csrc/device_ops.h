@@ -128,6 +128,19 @@ struct ops<cplx<double>> : complex_ops<double, uint64_t> {
 };
 
 // ---------------------------------------------------------------------------
+// 1/x rounded once, fast: v_rcp_f32 and one Newton step.  For every |x| in
+// [2^-125, 2^125] this equals the correctly rounded quotient 1/x; the
+// library's self-check (batchlu_check_reciprocal) compares the two over every
+// float of that range on the device.  Outside the range, callers divide.
+// ---------------------------------------------------------------------------
+__device__ inline float recip_fast(float x) {
+    const float r0 = __builtin_amdgcn_rcpf(x);
+    const float e = __builtin_fmaf(-x, r0, 1.0f);
+    return __builtin_fmaf(e, r0, r0);
+}
+__device__ inline bool recip_fast_ok(float ax) { return ax >= 0x1p-125f && ax <= 0x1p125f; }
+
+// ---------------------------------------------------------------------------
 // pivot keys: a candidate's key is (bits of its metric) + 1, every NaN
 // clamped to the bit pattern just above +inf (so all NaNs tie, above every
 // number, and the lowest position among them wins); non-candidates get 0.

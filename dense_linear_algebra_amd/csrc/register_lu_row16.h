@@ -166,15 +166,6 @@ __device__ inline int rec_off_dyn(int j) {
     return 4 * (q * (NBC + NRC) - (q * (q - 1)) / 2) + t * (NBC + NRC - q);
 }
 
-// 1/x rounded once: v_rcp_f32 and one Newton step agree with the IEEE
-// quotient for every |x| in [2^-125, 2^125] (checked exhaustively on the
-// device); outside that range the full division is taken.
-__device__ inline float recip_fast(float x) {
-    const float r0 = __builtin_amdgcn_rcpf(x);
-    const float e = __builtin_fmaf(-x, r0, 1.0f);
-    return __builtin_fmaf(e, r0, r0);
-}
-__device__ inline bool recip_fast_ok(float ax) { return ax >= 0x1p-125f && ax <= 0x1p125f; }
 // the reciprocal of a pivot, the same bits wherever it is formed
 __device__ inline float recip_step(float piv) {
     float r = recip_fast(piv);

@@ -155,6 +155,28 @@ int batchlu_select_tier(batchlu_dtype t, int op, int n, int nrhs, int batch);
  */
 int batchlu_set_tier(int tier);
 
+/*
+ * batchlu_check_reciprocal -- device self-check of the fast float reciprocal
+ * the register tiers use for pivots (BatchLAS "Blackwell" page, getrs tiny
+ * paragraph: one reciprocal per pivot instead of a division per element;
+ * the library forms it as v_rcp_f32 plus one Newton step wherever
+ * 2^-125 <= |x| <= 2^125 and divides elsewhere, and relies on the result
+ * being the correctly rounded 1/x there).
+ *   1 lo_bits, 2 hi_bits  the inclusive range of float bit patterns to test
+ *                         (hi_bits >= lo_bits, else -2)
+ *   3 mismatches          device uint64, in: 0; out: += number of inputs in
+ *                         the range whose fast reciprocal differs from the
+ *                         IEEE quotient 1/x (inputs outside the fast range
+ *                         are not counted: the library divides there)
+ *   4 first_bad           device uint32, in: 0xffffffff; out: the lowest
+ *                         such bit pattern (atomic minimum)
+ *   5 stream
+ * Diagnostic only; the factorisations never call it.
+ */
+int batchlu_check_reciprocal(unsigned int lo_bits, unsigned int hi_bits,
+                             unsigned long long* mismatches,
+                             unsigned int* first_bad, hipStream_t stream);
+
 /* Human-readable name of a status code. */
 const char* batchlu_status_string(int status);
 

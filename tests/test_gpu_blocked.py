@@ -169,3 +169,13 @@ def test_blocked_full_size_workloads(name):
     np.testing.assert_array_equal(gP[:, :w.n], oP)
     assert matrices_equal_bits(gA, oA, w.n, w.n, w.n, w.n * w.n, w.batch) == []
     assert matrices_equal_bits(gB, oB, w.n, w.nrhs, w.n, w.n * w.nrhs, w.batch) == []
+    # the two accuracy bounds of the target on a sample of the batch:
+    # ||PA - LU||_F / (n eps ||A||_F) <= 20 and the solve residual <= 20
+    sample = sorted({0, w.batch // 3, w.batch // 2, w.batch - 1})
+    for b in sample:
+        Am = oracle.matrix(A, b, w.n, w.n, w.n, w.n * w.n)
+        fr = oracle.factor_residual(Am, oracle.matrix(gA, b, w.n, w.n, w.n, w.n * w.n), gP[b, :w.n])
+        assert fr <= 20, f"matrix {b}: factor residual {fr}"
+        sr = oracle.solve_residual(Am, oracle.matrix(gB, b, w.n, w.nrhs, w.n, w.n * w.nrhs),
+                                   oracle.matrix(B, b, w.n, w.nrhs, w.n, w.n * w.nrhs))
+        assert sr <= 20, f"matrix {b}: solve residual {sr}"

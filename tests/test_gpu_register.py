@@ -190,6 +190,12 @@ def test_full_size_workloads(name):
     rng = np.random.default_rng(0)
     sample = sorted(set(rng.integers(0, w.batch, 64).tolist()) | {0, w.batch - 1})
     _check_solution(A, B, gB, w.n, w.nrhs, w.batch, oI, oB, sample=sample)
+    # the two accuracy bounds of the target on the same sample:
+    # ||PA - LU||_F / (n eps ||A||_F) <= 20 and the solve residual <= 20
+    for b in sample:
+        Am = oracle.matrix(A, b, w.n, w.n, w.n, w.n * w.n)
+        fr = oracle.factor_residual(Am, oracle.matrix(gA, b, w.n, w.n, w.n, w.n * w.n), gP[b, :w.n])
+        assert fr <= 20, f"matrix {b}: factor residual {fr}"
 
 
 def test_selected_tiers():

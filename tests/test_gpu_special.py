@@ -1,0 +1,195 @@
+"""GPU checks of the method's special cases: the hand-worked fixtures on every
+tier, exactly-zero pivots next to infinities and signed zeros, the device
+self-check of the fast reciprocal, and the largest order each blocked
+configuration accepts.  Every case is compared with the oracle (or with the
+fixture's hand-derived bits) through the C ABI."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import lu_inputs
+import oracle
+from gpu_support import bits, gesv_gpu, gpu_available, matrices_equal_bits, oracle_run, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    import torch
+    import dense_linear_algebra_amd as lib
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+DT = {"float32": np.float32, "float64": np.float64, "complex64": np.complex64, "complex128": np.complex128}
+
+
+@pytest.fixture(autouse=True)
+def _auto_tier():
+    if not gpu_available():
+        pytest.skip("needs a GPU")
+    lib.batchlu_set_tier(lib.TIER_AUTO)
+    yield
+    lib.batchlu_set_tier(lib.TIER_AUTO)
+
+
+def _num(v):
+    if isinstance(v, list):
+        return complex(_num(v[0]), _num(v[1]))
+    if isinstance(v, str):
+        if v.startswith("f32:0x"):
+            return float(np.array([int(v[4:], 16)], np.uint32).view(np.float32)[0])
+        if v.startswith("f64:0x"):
+            return float(np.array([int(v[4:], 16)], np.uint64).view(np.float64)[0])
+        if "*2^" in v:
+            m, e = v.split("*2^")
+            return float(np.ldexp(float(m), int(e)))
+        return float(v)
+    return float(v)
+
+
+def _mat(rows, dtype):
+    return np.array([[_num(x) for x in r] for r in rows], dtype=dtype)
+
+
+def _fixture_params():
+    with open(os.path.join(HERE, "golden", "hand_worked.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        for dt in c["dtypes"]:
+            for tier in ("tiny", "cta", "blocked"):
+                yield pytest.param(c, DT[dt], tier, id=f"{c['name']}-{dt}-{tier}")
+
+
+@pytest.mark.parametrize("case,dtype,tier", list(_fixture_params()))
+def test_hand_worked_fixture_on_tier(case, dtype, tier):
+    """Each hand-worked fixture (derived from the pages' conventions, not from
+    the oracle), batched 5 times, through one pinned tier: ipiv, info and LU
+    equal to the fixture bit for bit; with a right-hand side, X from getrs
+    equal to the fixture's X.  A tier that does not take the shape is
+    skipped."""
+    A = _mat(case["A"], dtype)
+    n = A.shape[0]
+    batch = 5
+    flat = np.concatenate([np.ascontiguousarray(A.T).reshape(-1)] * batch)
+    code = {"tiny": lib.TIER_TINY, "cta": lib.TIER_CTA, "blocked": lib.TIER_BLOCKED}[tier]
+    lib.batchlu_set_tier(code)
+    t = lib.dtype_code(np.dtype(dtype))
+    if lib.batchlu_select_tier(t, 0, n, 0, batch) != code:
+        pytest.skip(f"tier {tier} does not take n = {n}")
+    print(f"case fixture {case['name']} {np.dtype(dtype).name} {tier}", flush=True)
+    dA = to_dev(flat)
+    dP = torch.full((batch * n,), -7, dtype=torch.int32, device="cuda")
+    dI = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
+    lib.batchlu_getrf(t, n, dA, n, n * n, dP, n, dI, batch)
+    torch.cuda.synchronize()
+    gA, gP, gI = to_host(dA), to_host(dP).reshape(batch, n), to_host(dI)
+    for b in range(batch):
+        assert list(gP[b]) == case["ipiv"], f"matrix {b}"
+        assert int(gI[b]) == case["info"], f"matrix {b}"
+        if case["LU"] is not None:
+            got = oracle.matrix(gA, b, n, n, n, n * n)
+            assert np.array_equal(bits(got), bits(_mat(case["LU"], dtype))), f"matrix {b}: {got!r}"
+    if "B" not in case:
+        return
+    B = _mat(case["B"], dtype)
+    nr = B.shape[1]
+    flatB = np.concatenate([np.ascontiguousarray(B.T).reshape(-1)] * batch)
+    dB = to_dev(flatB)
+    lib.batchlu_getrs(t, "N", n, nr, dA, n, n * n, dP, n, dB, n, n * nr, batch)
+    torch.cuda.synchronize()
+    gB = to_host(dB)
+    for b in range(batch):
+        got = oracle.matrix(gB, b, n, nr, n, n * nr)
+        assert np.array_equal(bits(got), bits(_mat(case["X"], dtype))), f"matrix {b}: X {got!r}"
+
+
+def test_fast_reciprocal_is_correctly_rounded_everywhere_it_is_used():
+    """The register tiers form 1/pivot as v_rcp_f32 plus one Newton step
+    wherever 2^-125 <= |x| <= 2^125 and rely on it equalling the IEEE
+    quotient there.  Every float bit pattern is compared on the device
+    (both signs, the whole 32-bit range; outside the fast range the library
+    divides, so those inputs are not counted)."""
+    mism = torch.zeros(1, dtype=torch.int64, device="cuda")
+    first = torch.full((1,), -1, dtype=torch.int32, device="cuda")   # 0xffffffff
+    print("case reciprocal self-check over all 2^32 patterns", flush=True)
+    lib.batchlu_check_reciprocal(0, 0xFFFFFFFF, mism, first)
+    torch.cuda.synchronize()
+    n_bad = int(mism.item())
+    first_bad = int(first.item()) & 0xFFFFFFFF
+    assert n_bad == 0, f"{n_bad} mismatches, first at bits 0x{first_bad:08x}"
+
+
+def test_reciprocal_self_check_counts_what_it_should():
+    """The check itself reports differences: over a range entirely outside the
+    fast range nothing is counted, and an inverted range is refused."""
+    mism = torch.zeros(1, dtype=torch.int64, device="cuda")
+    first = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    # subnormals and the smallest normals (|x| < 2^-125): never the fast form
+    lib.batchlu_check_reciprocal(0x00000000, 0x01000000, mism, first)
+    torch.cuda.synchronize()
+    assert int(mism.item()) == 0
+    assert lib.batchlu_check_reciprocal(5, 4, mism, first, raise_on_error=False) == -2
+
+
+ZERO_PIVOT_CASES = [
+    (np.float32, 20), (np.float32, 45), (np.complex64, 45), (np.float64, 40),      # register tiers
+    (np.float32, 70), (np.float64, 70),                                           # one work-group blocked
+    (np.complex64, 70), (np.complex128, 70), (np.float32, 300), (np.float64, 300),  # multi-launch blocked
+    (np.complex64, 130), (np.complex128, 100),
+]
+
+
+@pytest.mark.parametrize("dtype,n", ZERO_PIVOT_CASES, ids=lambda v: getattr(v, "__name__", str(v)))
+def test_zero_pivot_next_to_infinity_and_signed_zeros(dtype, n):
+    """Exactly-zero pivots whose pivot row holds +inf and a 1 above a column
+    of -0 (lu_inputs.zero_pivot_problem): the step of a zero pivot changes
+    nothing beyond its own column, so no 0 * inf NaN and no +0 replacing -0
+    may appear.  ipiv, info and LU bit-identical to the oracle (NaN positions
+    compared, payloads not)."""
+    batch = 6
+    A, B = lu_inputs.zero_pivot_problem(500 + n, dtype, n, 2, batch)
+    print(f"case zero-pivot {np.dtype(dtype).name} n={n}", flush=True)
+    gA, _, gP, gI = gesv_gpu(lib, A, B, n, 2, batch, op="getrf")
+    oA, _, oP, oI, _ = oracle_run(A, B, n, 2, batch, op="getrf")
+    assert np.all(oI > 0)
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+
+
+@pytest.mark.parametrize("dtype,n", [(np.float32, 1100), (np.float64, 1030)],
+                         ids=lambda v: getattr(v, "__name__", str(v)))
+def test_zero_pivot_factors_through_the_blocked_solve(dtype, n):
+    """Orders above the one-launch solve (n > 1024) run the block-by-block
+    solve with MFMA updates.  On factors with exactly
+    zero pivots, infinities and signed zeros, X must equal the oracle's
+    solve on the same factors bit for bit (NaN positions compared)."""
+    batch, nrhs = 2, 3
+    A, B = lu_inputs.zero_pivot_problem(900 + n, dtype, n, nrhs, batch)
+    print(f"case zero-pivot getrs {np.dtype(dtype).name} n={n}", flush=True)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch, op="getrf+getrs")
+    oB = B.copy()
+    oracle.getrs(gA, n, n, n * n, gP[:, :n], oB, nrhs, n, n * nrhs, batch)
+    assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
+
+
+# largest order of each blocked configuration, a small batch each
+CAPACITY = [(np.float32, 2048), (np.float64, 2048), (np.complex64, 1024), (np.complex128, 1024)]
+
+
+@pytest.mark.parametrize("dtype,n", CAPACITY, ids=lambda v: getattr(v, "__name__", str(v)))
+def test_blocked_tier_at_its_largest_order(dtype, n):
+    """The largest order the blocked tier accepts for each type: ipiv, info
+    and LU bit-identical to the oracle, X bit-identical to the oracle's
+    solve, and one order more is refused with BATCHLU_ERR_CAPACITY."""
+    batch, nrhs = 1, 2
+    A, B = lu_inputs.random_problem(7000 + n, dtype, n, nrhs, batch)
+    print(f"case capacity {np.dtype(dtype).name} n={n}", flush=True)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch, op="getrf+getrs")
+    oA, oB, oP, oI, _ = oracle_run(A, B, n, nrhs, batch, op="getrf+getrs")
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+    assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
+    t = lib.dtype_code(np.dtype(dtype))
+    assert lib.batchlu_select_tier(t, 0, n + 1, 0, 1) == -101   # BATCHLU_ERR_CAPACITY
