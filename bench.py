@@ -50,7 +50,7 @@ KERNEL_SOURCES = {
     "sgesv_n32_r8_b32768": [_C + "register_lu_row16.h", _C + "device_ops.h"],
     "cgesv_n64_r16_b8192": [_C + "register_lu_kernel.h", _C + "device_ops.h"],
     "dgesv_n256_b1024": [_C + "blocked_fused.hip", _C + "device_ops.h"],
-    "sgetrf_sgetrs_n1024_r32_b64": [_C + "blocked_lu.hip", _C + "device_ops.h"],
+    "sgetrf_sgetrs_n1024_r32_b64": [_C + "blocked_lu_impl.h", _C + "device_ops.h"],
 }
 
 
@@ -121,14 +121,19 @@ def write_counter_summary(workload: str, kernel: str, fetch_db: str, write_db: s
     one and the bytes are per launch of it."""
     w = lu_inputs.WORKLOADS[workload]
     res = {"kernel": kernel, "workload": workload, "source_hash": source_hash(workload), "commands": list(commands)}
+    # several kernels may be named, separated by '|': their bytes are summed
+    # and divided by the dispatches of the first one (e.g. the launches of one
+    # blocked getrf per dispatch of its final interchange kernel)
+    names = kernel.split("|")
     per = {}
     for tag, db in (("fetch", fetch_db), ("write", write_db)):
         rows = _counter_rows(db)
         copies = [v for n, v in rows.values() if n.startswith("__amd_rocclr_copyBuffer")]
-        mine = [v for n, v in rows.values() if kernel in n]
-        if not copies or not mine:
-            raise SystemExit(f"{db}: no copy probe or no '{kernel}' dispatch")
-        per[tag] = (sum(mine) / len(mine), max(copies))
+        mine = [v for n, v in rows.values() if any(k in n for k in names)]
+        units = [v for n, v in rows.values() if names[0] in n]
+        if not copies or not units:
+            raise SystemExit(f"{db}: no copy probe or no '{names[0]}' dispatch")
+        per[tag] = (sum(mine) / len(units), max(copies))
     nbytes = copy_mb << 20
     fetch_scale = nbytes / (per["fetch"][1] * 1024.0)
     write_scale = nbytes / (per["write"][1] * 1024.0)
@@ -145,6 +150,68 @@ def write_counter_summary(workload: str, kernel: str, fetch_db: str, write_db: s
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
     print(path)
+
+
+def kernel_counter_table(dbs):
+    """Per kernel: dispatches and the mean of every counter per dispatch, from
+    one or more rocprofv3 --pmc databases; with the SQ busy counters also the
+    derived MFMA and VALU utilisation.  rocprofv3 reports a counter summed
+    over the GPU's instances, so GRBM_GUI_ACTIVE (per XCD) is divided by the
+    8 XCDs, as its 'max' reduction in the derived metrics assumes.  Printed
+    as a markdown table."""
+    import csv
+    import subprocess
+    import tempfile
+    per = {}
+    for db in dbs:
+        out = os.path.join(tempfile.mkdtemp(), "csv")
+        subprocess.run(["/opt/rocm/bin/rocpd2csv", "-i", os.path.abspath(db), "-d", out], check=True,
+                       capture_output=True, cwd="/tmp")
+        with open(os.path.join(out, "out_counter_collection_trace.csv")) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("batchlu::", "")
+                name = name[5:] if name.startswith("void ") else name
+                name = name.split("(")[0]
+                d = per.setdefault(name, {})
+                d.setdefault(r["Counter_Name"], {})[(db, r["Dispatch_Id"])] = float(r["Counter_Value"])
+    cols = sorted({c for d in per.values() for c in d})
+    derived = {"GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU"} <= set(cols)
+    head = ["kernel", "dispatches"] + cols + (["MFMA busy %", "VALU busy %"] if derived else [])
+    print("| " + " | ".join(head) + " |")
+    print("|" + "---|" * len(head))
+    for name, d in sorted(per.items()):
+        k = max(len(v) for v in d.values())
+        mean = {c: (sum(d[c].values()) / len(d[c]) if c in d else float("nan")) for c in cols}
+        row = [f"`{name}`", str(k)] + [f"{mean[c]:.4g}" for c in cols]
+        if derived:
+            g = mean["GRBM_GUI_ACTIVE"] / 8.0
+            row += [f"{100.0 * mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (g * 1024):.1f}",
+                    f"{100.0 * mean['SQ_ACTIVE_INST_VALU'] / 256 / g:.1f}"]
+        print("| " + " | ".join(row) + " |")
+
+
+def kernel_trace_table(db):
+    """Per kernel: calls, total ms, mean and median us and share of the
+    kernel time in one rocprofv3 --kernel-trace database (markdown)."""
+    import csv
+    import subprocess
+    import tempfile
+    out = os.path.join(tempfile.mkdtemp(), "csv")
+    subprocess.run(["/opt/rocm/bin/rocpd2csv", "-i", os.path.abspath(db), "-d", out], check=True,
+                   capture_output=True, cwd="/tmp")
+    per = {}
+    with open(os.path.join(out, "out_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("batchlu::", "")
+            name = name[5:] if name.startswith("void ") else name
+            name = name.split("(")[0]
+            per.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    total = sum(sum(v) for v in per.values())
+    print("| kernel | calls | total ms | mean us | median us | % |")
+    print("|---|---|---|---|---|---|")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{name}` | {len(v)} | {sum(v) * 1e-3:.3f} | {np.mean(v):.2f} | {np.median(v):.2f} | "
+              f"{100.0 * sum(v) / total:.1f} |")
 
 
 # ---------------------------------------------------------------------------
@@ -366,7 +433,17 @@ def main():
     ap.add_argument("--counters-summary", nargs=3, metavar=("KERNEL", "FETCH_DB", "WRITE_DB"),
                     help="write the HBM-traffic summary of KERNEL from two rocprofv3 --pmc databases "
                          "(FETCH_SIZE, WRITE_SIZE) taken with --copy-probe-mb; no GPU needed")
+    ap.add_argument("--kernel-counters", nargs="+", metavar="DB",
+                    help="print per-kernel means of the counters in rocprofv3 --pmc databases; no GPU needed")
+    ap.add_argument("--trace-summary", metavar="DB",
+                    help="print per-kernel times of a rocprofv3 --kernel-trace database; no GPU needed")
     args = ap.parse_args()
+    if args.trace_summary:
+        kernel_trace_table(args.trace_summary)
+        return
+    if args.kernel_counters:
+        kernel_counter_table(args.kernel_counters)
+        return
     if args.counters_summary:
         kern, fdb, wdb = args.counters_summary
         mb = args.copy_probe_mb or 256

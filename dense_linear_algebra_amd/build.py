@@ -11,6 +11,7 @@ from __future__ import annotations
 import concurrent.futures
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,13 +35,30 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+def _deps(src: str, seen=None) -> set:
+    """src and every file it includes with #include "..." (transitively)."""
+    seen = set() if seen is None else seen
+    if src in seen or not os.path.exists(src):
+        return seen
+    seen.add(src)
+    with open(src) as f:
+        for line in f:
+            m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+            if m:
+                for d in (os.path.dirname(src), CSRC, INCLUDE):
+                    cand = os.path.normpath(os.path.join(d, m.group(1)))
+                    if os.path.exists(cand):
+                        _deps(cand, seen)
+                        break
+    return seen
+
+
 def _stale(src: str, obj: str) -> bool:
-    """True when obj is missing or older than src or any header it may include."""
+    """True when obj is missing or older than src or a file it includes."""
     if not os.path.exists(obj):
         return True
     t = os.path.getmtime(obj)
-    deps = [src] + glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(INCLUDE, "*.h"))
-    return any(os.path.getmtime(d) > t for d in deps)
+    return any(os.path.getmtime(d) > t for d in _deps(src))
 
 
 def _compile(src: str, verbose: bool, extra=(), incremental=False):

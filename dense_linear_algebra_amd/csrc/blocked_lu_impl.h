@@ -1,4 +1,4 @@
-// blocked_lu.hip -- blocked right-looking LU (panel width 32) and the blocked
+// blocked_lu_impl.h -- blocked right-looking LU (panel width 32) and the blocked
 // LU solve, for matrices too large for the register tiers.
 //
 // BatchLAS "LU" page, blocked-getrf and register-panel paragraphs, and the
@@ -22,6 +22,8 @@
 // substitution run block by block (a 32-row triangular solve, then a GEMM
 // update of the remaining rows), preserving the plain order of operations
 // (ascending k forward, descending k backward, true division by u_kk).
+#pragma once
+
 #include <type_traits>
 
 #include "device_ops.h"
@@ -841,6 +843,176 @@ __global__ void __launch_bounds__(256) update_strip_kernel(T* A, int lda, long l
     }
 }
 
+// Complex getrf trailing update A22 -= L21 U12 on real MFMAs (K = 32
+// complex steps, ascending).  A complex z -= x*y is four real fused
+// multiply-adds in a fixed order (GEMM page, POD complex paragraph): the real
+// part takes -xr*yr then +xi*yi, the imaginary part -xr*yi then -xi*yr.
+// Interleaving each complex k into two real k' = 2k + h turns both parts
+// into real products whose terms arrive in exactly that order:
+//   re: sum over k' of Ure[c][k'] * Lre[k'][i], Ure = (u.re, u.im), Lre = (-l.re, l.im)
+//   im: sum over k' of Uim[c][k'] * Lim[k'][i], Uim = (u.im, u.re), Lim = (-l.re, -l.im)
+// and an MFMA chain in ascending k' accumulates like a chain of fused
+// multiply-adds in k' order, so every element sees the unblocked operation
+// sequence.  Same C^T arrangement and strip walk as update_strip_kernel: one
+// work-group per strip of 32*TB rows walks the strip's 64-column tiles, the
+// L operands stay in registers, the next U tile is staged into LDS and the
+// next C tile loaded while the current one runs.  A zero pivot among the
+// panel's 32 leaves its k out on the VALU, as in the unblocked order.
+template <typename R>
+struct CplxStrip {
+    static constexpr int TB = sizeof(R) == 4 ? 2 : 1;   // 16-row blocks per wavefront
+    static constexpr int SH = 32 * TB;                   // strip height
+};
+
+template <typename R>
+__global__ void __launch_bounds__(256) update_strip_cplx_kernel(cplx<R>* A, int lda, long long sA, int j0, int M,
+                                                                int mstrips)
+{
+    using T = cplx<R>;
+    using O = ops<T>;
+    using V = typename std::conditional<sizeof(R) == 4, f32x4, f64x4>::type;
+    constexpr int TB = CplxStrip<R>::TB, SH = CplxStrip<R>::SH;
+    constexpr int KP = 2 * NBP;                              // real k' per panel
+    constexpr int UP = 64 + (sizeof(R) == 4 ? 2 : 1);         // padded row of a staged U tile
+    __shared__ __attribute__((aligned(16))) T Us[2][NBP][UP];
+    __shared__ unsigned zmask;
+    const int tid = threadIdx.x;
+    const long long mat = blockIdx.x / mstrips;
+    const int r0 = (int)(blockIdx.x % mstrips) * SH;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wr = wave & 1, wc = wave >> 1;
+    const int li = lane & 15, lk = lane >> 4;
+    const bool hodd = (lk & 1) != 0;                          // this lane's k' = 2k + 1
+    T* base = A + mat * sA;
+    const T* Lp = base + j0 + NBP + (long long)j0 * lda;             // L21
+    const T* Up = base + j0 + (long long)(j0 + NBP) * lda;           // U12
+    T* Cp = base + j0 + NBP + (long long)(j0 + NBP) * lda;           // A22
+    const int N = M;
+    const int nct = (N + 63) / 64;
+    if (tid == 0) zmask = 0;
+    __syncthreads();
+    if (tid < NBP && O::metric(base[j0 + tid + (long long)(j0 + tid) * lda]) == R(0)) atomicOr(&zmask, 1u << tid);
+    // a U tile (32 complex rows x 64 columns) into the stage
+    auto load_u = [&](int ct, T (&v)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = tid + 256 * u, k = e & (NBP - 1), c = ct * 64 + (e >> 5);
+            v[u] = c < N ? Up[k + (long long)c * lda] : O::zero();
+        }
+    };
+    auto put_u = [&](int b, const T (&v)[8]) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = tid + 256 * u;
+            Us[b][e & (NBP - 1)][e >> 5] = v[u];
+        }
+    };
+    {
+        T v[8];
+        load_u(0, v);
+        put_u(0, v);
+    }
+    __syncthreads();
+    if (zmask != 0) {
+        // a zero pivot in this panel: plain k loop without that k (rare)
+#pragma unroll 1
+        for (int e = tid; e < SH * N; e += 256) {
+            const int i = r0 + e % SH, j = e / SH;
+            if (i >= M) continue;
+            T c = Cp[i + (long long)j * lda];
+#pragma unroll 1
+            for (int k = 0; k < NBP; ++k)
+                if (!((zmask >> k) & 1u)) O::fms(c, Lp[i + (long long)k * lda], Up[k + (long long)j * lda]);
+            Cp[i + (long long)j * lda] = c;
+        }
+        return;
+    }
+    // L21 operands of this wavefront's row blocks: lane (li, lk) holds row
+    // i = block + li at k' = 4 s2 + lk, i.e. complex k = 2 s2 + lk / 2
+    R lre[TB][KP / 4], lim[TB][KP / 4];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+        const int i = r0 + wr * 16 * TB + t * 16 + li;
+#pragma unroll
+        for (int s2 = 0; s2 < KP / 4; ++s2) {
+            const int k = 2 * s2 + (lk >> 1);
+            const T l = i < M ? Lp[i + (long long)k * lda] : O::zero();
+            lre[t][s2] = hodd ? l.im : -l.re;
+            lim[t][s2] = hodd ? -l.im : -l.re;
+        }
+    }
+    auto load_c = [&](int ct, V (&cr)[TB][2], V (&ci)[TB][2]) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = r0 + wr * 16 * TB + t * 16 + li;
+                    const int j = ct * 64 + wc * 32 + b * 16 + mfma_row_t<R>(lk, r);
+                    const T z = (i < M && j < N) ? Cp[i + (long long)j * lda] : O::zero();
+                    cr[t][b][r] = z.re;
+                    ci[t][b][r] = z.im;
+                }
+    };
+    V cr[TB][2], ci[TB][2];
+    load_c(0, cr, ci);
+#pragma unroll 1
+    for (int ct = 0; ct < nct; ++ct) {
+        const int buf = ct & 1;
+        T un[8];
+        V nr[TB][2], ni[TB][2];
+        const bool more = ct + 1 < nct;
+        if (more) {
+            load_u(ct + 1, un);
+            load_c(ct + 1, nr, ni);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int c = wc * 32 + b * 16 + li;
+            // k' = 4 s2 + lk is complex k = 2 s2 + lk / 2, part lk % 2
+            R ur[KP / 4], ui[KP / 4];
+#pragma unroll
+            for (int s2 = 0; s2 < KP / 4; ++s2) {
+                const T z = Us[buf][2 * s2 + (lk >> 1)][c];
+                ur[s2] = hodd ? z.im : z.re;
+                ui[s2] = hodd ? z.re : z.im;
+            }
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                V accr = cr[t][b], acci = ci[t][b];
+#pragma unroll
+                for (int s2 = 0; s2 < KP / 4; ++s2) {
+                    if constexpr (sizeof(R) == 4) {
+                        accr = __builtin_amdgcn_mfma_f32_16x16x4f32(ur[s2], lre[t][s2], accr, 0, 0, 0);
+                        acci = __builtin_amdgcn_mfma_f32_16x16x4f32(ui[s2], lim[t][s2], acci, 0, 0, 0);
+                    } else {
+                        accr = __builtin_amdgcn_mfma_f64_16x16x4f64(ur[s2], lre[t][s2], accr, 0, 0, 0);
+                        acci = __builtin_amdgcn_mfma_f64_16x16x4f64(ui[s2], lim[t][s2], acci, 0, 0, 0);
+                    }
+                }
+                const int i = r0 + wr * 16 * TB + t * 16 + li;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = ct * 64 + wc * 32 + b * 16 + mfma_row_t<R>(lk, r);
+                    if (i < M && j < N) Cp[i + (long long)j * lda] = T{accr[r], acci[r]};
+                }
+            }
+        }
+        if (more) {
+            put_u(buf ^ 1, un);
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    cr[t][b] = nr[t][b];
+                    ci[t][b] = ni[t][b];
+                }
+        }
+        __syncthreads();
+    }
+}
+
 // VALU version (complex types): each thread owns a 4 x 4 block of the tile.
 // With Dm (the getrf trailing update) a k whose pivot -- diagonal entry k of
 // the K x K block at Dm -- is exactly zero is left out, as in the unblocked
@@ -1110,11 +1282,13 @@ hipError_t getrf_t(const Problem& p, hipStream_t s) {
             hipLaunchKernelGGL((update_strip_kernel<T>), dim3((unsigned)((long long)ms * p.batch)), dim3(256), 0, s,
                                A, p.lda, p.sA, j0, rest, ms);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-        } else if ((e = launch_gemm<T>(A + j0 + w + (long long)j0 * p.lda, p.lda, p.sA,
-                                       A + j0 + (long long)(j0 + w) * p.lda, p.lda, p.sA,
-                                       A + j0 + w + (long long)(j0 + w) * p.lda, p.lda, p.sA, rest, rest, w, p.batch,
-                                       1, nullptr, s, A + j0 + (long long)j0 * p.lda, p.lda, p.sA)) != hipSuccess) {
-            return e;
+        } else {
+            using R = typename ops<T>::R;
+            constexpr int SH = CplxStrip<R>::SH;
+            const int ms = (rest + SH - 1) / SH;
+            hipLaunchKernelGGL((update_strip_cplx_kernel<R>), dim3((unsigned)((long long)ms * p.batch)), dim3(256), 0,
+                               s, A, p.lda, p.sA, j0, rest, ms);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
     if (n > NBP) {
@@ -1170,38 +1344,5 @@ hipError_t getrs_t(const Problem& p, hipStream_t s) {
 }
 
 }  // namespace
-
-bool blocked_supported(int dtype, int n) {
-    // the largest orders the parity tests run: float and double 2048, the
-    // complex types 1024 (double panels above 1024 rows and complex double
-    // panels above 512 rows hold four rows per thread and spill registers:
-    // correct, slower)
-    const int cap = (dtype == R32 || dtype == R64) ? 2048 : 1024;
-    return n >= 1 && n <= cap;
-}
-
-hipError_t blocked_getrf(int dtype, const Problem& p, hipStream_t s) {
-    if (!blocked_supported(dtype, p.n)) return hipErrorInvalidValue;
-    // real orders up to 256: the whole blocked sequence in one work-group
-    if (blocked_fused_supported(dtype, p.n, p.lda)) return blocked_fused_getrf(dtype, p, s);
-    switch (dtype) {
-    case R32: return getrf_t<float>(p, s);
-    case R64: return getrf_t<double>(p, s);
-    case C64: return getrf_t<cplx<float>>(p, s);
-    case C128: return getrf_t<cplx<double>>(p, s);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t blocked_getrs(int dtype, const Problem& p, hipStream_t s) {
-    if (!blocked_supported(dtype, p.n)) return hipErrorInvalidValue;
-    switch (dtype) {
-    case R32: return getrs_t<float>(p, s);
-    case R64: return getrs_t<double>(p, s);
-    case C64: return getrs_t<cplx<float>>(p, s);
-    case C128: return getrs_t<cplx<double>>(p, s);
-    default: return hipErrorInvalidValue;
-    }
-}
 
 }  // namespace batchlu

@@ -1,0 +1,10 @@
+// blocked_lu_r64.hip -- blocked-tier instantiations for one data type
+// (split per type so the large unrolled panels compile in parallel).
+#include "blocked_lu_impl.h"
+
+namespace batchlu {
+
+hipError_t blocked_getrf_r64(const Problem& p, hipStream_t s) { return getrf_t<double>(p, s); }
+hipError_t blocked_getrs_r64(const Problem& p, hipStream_t s) { return getrs_t<double>(p, s); }
+
+}  // namespace batchlu
