@@ -137,3 +137,27 @@ def zero_pivot_problem(seed: int, dtype, n: int, nrhs: int, batch: int):
     A = np.concatenate(mats) if mats else np.zeros(0, dtype)
     B = draw(rng, dtype, batch * n * nrhs)
     return A, B
+
+
+def spd_problem(seed: int, dtype, n: int, nrhs: int, batch: int):
+    """Hermitian (real: symmetric) positive definite matrices and right-hand
+    sides, both triangles stored.
+
+    Matrix b is (G G^H) / n + I with G iid uniform[-1, 1] (complex: both
+    parts), formed in double precision, made exactly Hermitian as (M + M^H)/2
+    and then rounded to ``dtype`` (rounding commutes with conjugation, so the
+    stored matrix is exactly Hermitian; its diagonal is real).  Its spectrum
+    lies in [1, about 1 + 4n/3], so every matrix is well conditioned.  B is
+    iid uniform[-1, 1]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt = np.dtype(dtype)
+    wide = np.complex128 if dt.kind == "c" else np.float64
+    G = draw(rng, wide, batch * n * n).reshape(batch, n, n)
+    M = np.matmul(G, np.conj(np.swapaxes(G, 1, 2))) / max(n, 1) + np.eye(n)
+    M = (M + np.conj(np.swapaxes(M, 1, 2))) / 2
+    if dt.kind == "c":
+        idx = np.arange(n)
+        M[:, idx, idx] = M[:, idx, idx].real
+    A = np.ascontiguousarray(np.swapaxes(M, 1, 2)).reshape(-1).astype(dt)   # column-major
+    B = draw(rng, dt, batch * n * nrhs)
+    return A, B

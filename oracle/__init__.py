@@ -1,13 +1,15 @@
-"""CPU oracle for batched LU with partial pivoting, getrs and gesv.
+"""CPU oracle for batched LU with partial pivoting, getrs and gesv, and for
+batched Cholesky (potrf, potrs, posv).
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only callers.  The product library never imports it,
 and it imports nothing from the product package.
 
-The arithmetic lives in ``lu_oracle.c`` (plain C, working precision, explicit
-fma, built with ``-ffp-contract=off``); this module builds and loads it and
-adds numpy helpers for unpacking factors and for residual checks.  Which
-passage of the BatchLAS "LU" page each step follows is stated in the C file.
+The arithmetic lives in ``lu_oracle.c`` and ``chol_oracle.c`` (plain C,
+working precision, explicit fma, built with ``-ffp-contract=off``); this
+module builds and loads them and adds numpy helpers for unpacking factors and
+for residual checks.  Which passage of the BatchLAS pages each step follows
+is stated in the C files.
 """
 from __future__ import annotations
 
@@ -19,7 +21,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "lu_oracle.c")
+_SRCS = [os.path.join(_HERE, "lu_oracle.c"), os.path.join(_HERE, "chol_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -29,11 +31,13 @@ _CODE_OF = {np.dtype(v[1]): v[0] for v in DTYPES.values()}
 
 
 def build(force: bool = False) -> str:
-    """Compile lu_oracle.c into liboracle.so with gcc (no fused contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    """Compile the oracle's C sources into liboracle.so with gcc (no fused
+    contraction)."""
+    stale = not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(s) for s in _SRCS)
+    if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-               "-pthread", _SRC, "-o", tmp, "-lm"]
+               "-pthread"] + _SRCS + ["-o", tmp, "-lm"]
         subprocess.check_call(cmd)
         os.replace(tmp, _LIB)
     return _LIB
@@ -57,6 +61,8 @@ def _load():
             lib.oracle_getri_batch.restype = i32
             lib.oracle_gesv_batch.argtypes = [i32, i32, i32, vp, i32, i64, ip, i64, vp, i32, i64, ip, dp, i32, i32]
             lib.oracle_gesv_batch.restype = i32
+            lib.oracle_chol_batch.argtypes = [i32, i32, i32, i32, i32, vp, i32, i64, ip, vp, i32, i64, i32, i32]
+            lib.oracle_chol_batch.restype = i32
             _lib = lib
     return _lib
 
@@ -138,6 +144,50 @@ def gesv(A, n, lda, strideA, B, nrhs, ldb, strideB, batch, want_margins=False, n
     return ipiv[:, :max(n, 0)], info, margins, used
 
 
+def _uplo(uplo):
+    u = uplo.upper()
+    if u not in ("L", "U"):
+        raise ValueError("uplo must be 'L' or 'U'")
+    return 1 if u == "U" else 0
+
+
+def potrf(A, n, lda, strideA, batch, uplo="L", nthreads=0):
+    """Cholesky factor of ``batch`` Hermitian positive definite matrices in
+    place: 'L' overwrites the lower triangle with L (A = L L^H), 'U' the
+    upper with U (A = U^H U); the other triangle is neither read nor written.
+    Returns ``(info, threads_used)``; info[b] = j + 1 for the first column
+    whose diagonal value is not positive (the factorisation stops there)."""
+    if batch > 0 and n > 0:
+        _check_flat(A, (batch - 1) * strideA + (n - 1) * lda + n, "A")
+    info = np.zeros(max(batch, 0), np.int32)
+    used = _load().oracle_chol_batch(0, _code(A), _uplo(uplo), n, 0, _ptr(A), lda, strideA, _ptr(info),
+                                     None, 1, 0, batch, nthreads)
+    return info, used
+
+
+def potrs(F, n, lda, strideA, B, nrhs, ldb, strideB, batch, uplo="L", nthreads=0):
+    """Solve A X = B in place of ``B`` from the Cholesky factor in ``F``."""
+    if batch > 0 and n > 0 and nrhs > 0:
+        _check_flat(B, (batch - 1) * strideB + (nrhs - 1) * ldb + n, "B")
+        if F.dtype != B.dtype:
+            raise TypeError("factor and B dtypes differ")
+    return _load().oracle_chol_batch(1, _code(B), _uplo(uplo), n, nrhs, _ptr(F), lda, strideA, None,
+                                     _ptr(B), ldb, strideB, batch, nthreads)
+
+
+def posv(A, n, lda, strideA, B, nrhs, ldb, strideB, batch, uplo="L", nthreads=0):
+    """potrf, then potrs for every matrix whose info is 0 (B left as is
+    otherwise).  Returns ``(info, threads_used)``."""
+    if batch > 0 and n > 0:
+        _check_flat(A, (batch - 1) * strideA + (n - 1) * lda + n, "A")
+        if nrhs > 0:
+            _check_flat(B, (batch - 1) * strideB + (nrhs - 1) * ldb + n, "B")
+    info = np.zeros(max(batch, 0), np.int32)
+    used = _load().oracle_chol_batch(2, _code(A), _uplo(uplo), n, nrhs, _ptr(A), lda, strideA, _ptr(info),
+                                     _ptr(B), ldb, strideB, batch, nthreads)
+    return info, used
+
+
 # ---------------------------------------------------------------------------
 # views and checks (numpy, double or extended precision)
 # ---------------------------------------------------------------------------
@@ -209,3 +259,31 @@ def solve_residual(A, X, B):
         num = np.max(np.abs(R[:, j]))
         worst = max(worst, float(num / den) if den > 0 else float(num))
     return worst
+
+
+def hermitian_from(A, uplo="L"):
+    """The full Hermitian matrix whose named triangle is that of ``A`` (the
+    diagonal's imaginary part is dropped, as potrf never reads it)."""
+    n = A.shape[0]
+    T = np.tril(A) if uplo.upper() == "L" else np.triu(A).conj().T
+    H = T + np.tril(T, -1).conj().T
+    H[np.diag_indices(n)] = H.diagonal().real
+    return H
+
+
+def chol_factor(F, uplo="L"):
+    """The lower factor L (A = L L^H) held in the named triangle of ``F``."""
+    return np.tril(F) if uplo.upper() == "L" else np.triu(F).conj().T
+
+
+def chol_residual(A, F, uplo="L"):
+    """||A - L L^H||_F / (n eps ||A||_F) in wider precision, A taken as the
+    Hermitian matrix of its named triangle."""
+    n = A.shape[0]
+    if n == 0:
+        return 0.0
+    H = _wide(hermitian_from(A, uplo))
+    L = _wide(chol_factor(F, uplo))
+    num = np.sqrt(np.sum(np.abs(H - L @ L.conj().T) ** 2))
+    den = n * eps_of(A.dtype) * np.sqrt(np.sum(np.abs(H) ** 2))
+    return float(num / den) if den > 0 else float(num)

@@ -31,7 +31,7 @@ def _blocked_tier():
     lib.batchlu_set_tier(lib.TIER_AUTO)
 
 
-CASES = ([(np.float32, n) for n in (1, 7, 32, 33, 64, 65, 100, 161, 256, 290, 520)]
+CASES = ([(np.float32, n) for n in (1, 7, 32, 33, 64, 65, 100, 161, 256, 257, 290, 384, 520, 700)]
          + [(np.float64, n) for n in (31, 64, 96, 130, 256, 300)]
          + [(np.complex64, n) for n in (40, 64, 100, 130, 200, 300)]
          + [(np.complex128, n) for n in (33, 70, 100, 161, 257)])
