@@ -1,12 +1,13 @@
-"""Batched LU with partial pivoting (getrf), LU solve (getrs) and gesv on
-AMD Instinct MI355X (gfx950): hand-written HIP kernels behind a C ABI
-(include/batchlu.h), with a thin ctypes binding of the same names."""
+"""Batched LU with partial pivoting (getrf), LU solve (getrs), gesv and getri,
+and batched Cholesky (potrf, potrs, posv) on AMD Instinct MI355X (gfx950):
+hand-written HIP kernels behind a C ABI (include/batchlu.h), with a thin
+ctypes binding of the same names."""
 from ._binding import (C64, C128, R32, R64, TIER_AUTO, TIER_BLOCKED, TIER_CTA, TIER_NAMES, TIER_TINY,
                        BatchLUError, batchlu_check_reciprocal, batchlu_gesv, batchlu_getrf, batchlu_getri,
-                       batchlu_getrs, batchlu_select_tier, batchlu_set_tier, dtype_code, load, status_string,
-                       version)
+                       batchlu_getrs, batchlu_posv, batchlu_potrf, batchlu_potrs, batchlu_select_tier,
+                       batchlu_set_tier, dtype_code, load, status_string, version)
 
 __all__ = ["R32", "R64", "C64", "C128", "TIER_AUTO", "TIER_TINY", "TIER_CTA", "TIER_BLOCKED", "TIER_NAMES",
            "BatchLUError", "batchlu_check_reciprocal", "batchlu_getrf", "batchlu_getrs", "batchlu_getri",
-           "batchlu_gesv", "batchlu_select_tier", "batchlu_set_tier", "dtype_code", "load", "status_string",
-           "version"]
+           "batchlu_gesv", "batchlu_potrf", "batchlu_potrs", "batchlu_posv", "batchlu_select_tier",
+           "batchlu_set_tier", "dtype_code", "load", "status_string", "version"]

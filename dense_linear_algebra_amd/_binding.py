@@ -42,6 +42,9 @@ def load():
     lib.batchlu_getrs.argtypes = [i32, ch, i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, i32, vp]
     lib.batchlu_gesv.argtypes = [i32, i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, vp, i32, vp]
     lib.batchlu_getri.argtypes = [i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, i32, vp]
+    lib.batchlu_potrf.argtypes = [i32, ch, i32, vp, i32, i64, vp, i32, vp]
+    lib.batchlu_potrs.argtypes = [i32, ch, i32, i32, vp, i32, i64, vp, i32, i64, i32, vp]
+    lib.batchlu_posv.argtypes = [i32, ch, i32, i32, vp, i32, i64, vp, i32, i64, vp, i32, vp]
     lib.batchlu_check_reciprocal.argtypes = [ctypes.c_uint, ctypes.c_uint, vp, vp, vp]
     lib.batchlu_check_reciprocal.restype = i32
     lib.batchlu_select_tier.argtypes = [i32, i32, i32, i32, i32]
@@ -50,8 +53,8 @@ def load():
     lib.batchlu_status_string.restype = ctypes.c_char_p
     lib.batchlu_version.argtypes = []
     lib.batchlu_version.restype = ctypes.c_char_p
-    for f in ("batchlu_getrf", "batchlu_getrs", "batchlu_gesv", "batchlu_getri", "batchlu_select_tier",
-              "batchlu_set_tier"):
+    for f in ("batchlu_getrf", "batchlu_getrs", "batchlu_gesv", "batchlu_getri", "batchlu_potrf", "batchlu_potrs",
+              "batchlu_posv", "batchlu_select_tier", "batchlu_set_tier"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -119,6 +122,28 @@ def batchlu_gesv(t, n, nrhs, A, lda, strideA, ipiv, strideP, B, ldb, strideB, in
     st = load().batchlu_gesv(t, n, nrhs, _ptr(A), lda, strideA, _ptr(ipiv), strideP, _ptr(B), ldb, strideB,
                              _ptr(info), batch, _stream(stream))
     return _check("batchlu_gesv", st, raise_on_error)
+
+
+def _uplo(uplo):
+    return uplo.encode() if isinstance(uplo, str) else bytes([uplo])
+
+
+def batchlu_potrf(t, uplo, n, A, lda, strideA, info, batch, stream=None, raise_on_error=True):
+    st = load().batchlu_potrf(t, _uplo(uplo), n, _ptr(A), lda, strideA, _ptr(info), batch, _stream(stream))
+    return _check("batchlu_potrf", st, raise_on_error)
+
+
+def batchlu_potrs(t, uplo, n, nrhs, A, lda, strideA, B, ldb, strideB, batch, stream=None, raise_on_error=True):
+    st = load().batchlu_potrs(t, _uplo(uplo), n, nrhs, _ptr(A), lda, strideA, _ptr(B), ldb, strideB, batch,
+                              _stream(stream))
+    return _check("batchlu_potrs", st, raise_on_error)
+
+
+def batchlu_posv(t, uplo, n, nrhs, A, lda, strideA, B, ldb, strideB, info, batch, stream=None,
+                 raise_on_error=True):
+    st = load().batchlu_posv(t, _uplo(uplo), n, nrhs, _ptr(A), lda, strideA, _ptr(B), ldb, strideB, _ptr(info),
+                             batch, _stream(stream))
+    return _check("batchlu_posv", st, raise_on_error)
 
 
 def batchlu_check_reciprocal(lo_bits, hi_bits, mismatches, first_bad, stream=None, raise_on_error=True):

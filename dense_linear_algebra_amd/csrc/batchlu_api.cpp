@@ -208,6 +208,102 @@ int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda, long long s
     return run_getrs(tier, t, p, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Cholesky.  Tiers: the register kernel (TINY and CTA pins both name it),
+// else the blocked driver; posv fuses the solve in the register kernel for
+// nrhs <= 16 and otherwise composes potrf with the one-launch solve.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+bool valid_uplo(char u) { return u == 'L' || u == 'l' || u == 'U' || u == 'u'; }
+bool is_upper(char u) { return u == 'U' || u == 'u'; }
+
+int chol_tier(int t, int n) {
+    const int pin = tier_pin();
+    const bool reg = chol_register_supported(t, n), blk = chol_blocked_supported(t, n);
+    if (pin == BATCHLU_TIER_TINY || pin == BATCHLU_TIER_CTA) return reg ? pin : BATCHLU_ERR_CAPACITY;
+    if (pin == BATCHLU_TIER_BLOCKED) return blk ? pin : BATCHLU_ERR_CAPACITY;
+    return reg ? BATCHLU_TIER_CTA : blk ? BATCHLU_TIER_BLOCKED : BATCHLU_ERR_CAPACITY;
+}
+
+int run_potrf(int tier, int t, const Problem& p, hipStream_t s) {
+    if (tier == BATCHLU_TIER_BLOCKED) return status_of(chol_blocked_launch(t, p, s));
+    return status_of(chol_register_launch(t, p, false, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int batchlu_potrf(batchlu_dtype t, char uplo, int n, void* A, int lda, long long strideA, int* info, int batch,
+                  hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (!valid_uplo(uplo)) return -2;
+    if (n < 0) return -3;
+    if (lda < (n > 1 ? n : 1)) return -5;
+    if (batch < 0) return -8;
+    if (batch > 1 && strideA < (long long)lda * n) return -6;
+    if (n == 0 || batch == 0) return BATCHLU_OK;
+    if (!A) return -4;
+    if (!info) return -7;
+    const int tier = chol_tier(t, n);
+    if (tier < 0) return tier;
+    Problem p;
+    p.n = n; p.batch = batch; p.A = A; p.lda = lda; p.sA = strideA; p.info = info; p.upper = is_upper(uplo);
+    return run_potrf(tier, t, p, stream);
+}
+
+int batchlu_potrs(batchlu_dtype t, char uplo, int n, int nrhs, const void* A, int lda, long long strideA, void* B,
+                  int ldb, long long strideB, int batch, hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (!valid_uplo(uplo)) return -2;
+    if (n < 0) return -3;
+    if (nrhs < 0) return -4;
+    if (lda < (n > 1 ? n : 1)) return -6;
+    if (ldb < (n > 1 ? n : 1)) return -9;
+    if (batch < 0) return -11;
+    if (batch > 1 && strideA < (long long)lda * n) return -7;
+    if (batch > 1 && strideB < (long long)ldb * nrhs) return -10;
+    if (n == 0 || nrhs == 0 || batch == 0) return BATCHLU_OK;
+    if (!A) return -5;
+    if (!B) return -8;
+    if (!chol_solve_supported(t, n)) return BATCHLU_ERR_CAPACITY;
+    Problem p;
+    p.n = n; p.nrhs = nrhs; p.batch = batch; p.A = const_cast<void*>(A); p.lda = lda; p.sA = strideA;
+    p.B = B; p.ldb = ldb; p.sB = strideB; p.upper = is_upper(uplo);
+    return status_of(chol_solve_launch(t, p, stream));
+}
+
+int batchlu_posv(batchlu_dtype t, char uplo, int n, int nrhs, void* A, int lda, long long strideA, void* B, int ldb,
+                 long long strideB, int* info, int batch, hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (!valid_uplo(uplo)) return -2;
+    if (n < 0) return -3;
+    if (nrhs < 0) return -4;
+    if (lda < (n > 1 ? n : 1)) return -6;
+    if (ldb < (n > 1 ? n : 1)) return -9;
+    if (batch < 0) return -12;
+    if (batch > 1 && strideA < (long long)lda * n) return -7;
+    if (batch > 1 && strideB < (long long)ldb * nrhs) return -10;
+    if (n == 0 || batch == 0) return BATCHLU_OK;
+    if (!A) return -5;
+    if (nrhs > 0 && !B) return -8;
+    if (!info) return -11;
+    const int tier = chol_tier(t, n);
+    if (tier < 0) return tier;
+    if (nrhs > 0 && !chol_solve_supported(t, n)) return BATCHLU_ERR_CAPACITY;
+    Problem p;
+    p.n = n; p.nrhs = nrhs; p.batch = batch; p.A = A; p.lda = lda; p.sA = strideA; p.info = info;
+    p.B = B; p.ldb = ldb; p.sB = strideB; p.upper = is_upper(uplo);
+    if (tier != BATCHLU_TIER_BLOCKED && nrhs > 0 && nrhs <= 16)
+        return status_of(chol_register_launch(t, p, true, stream));
+    const int st = run_potrf(tier, t, p, stream);
+    if (st != BATCHLU_OK || nrhs == 0) return st;
+    return status_of(chol_solve_launch(t, p, stream));   // skips matrices whose info > 0
+}
+
 int batchlu_select_tier(batchlu_dtype t, int op, int n, int nrhs, int batch) {
     if (!valid_dtype(t)) return -1;
     if (op < OP_GETRF || op > OP_GESV) return -2;

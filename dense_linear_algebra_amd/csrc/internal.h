@@ -19,6 +19,7 @@ struct Problem {
     void* B = nullptr;  int ldb = 0;  long long sB = 0;
     int trans = 0;      // getrs: 0 solves A X = B, 1 A^T X = B, 2 A^H X = B
     bool inverse = false;   // getri: B is the output C; the solve runs on the identity
+    bool upper = false;     // Cholesky: the factor lives in the upper triangle (A = U^H U)
 };
 
 enum Mode { MODE_GETRF = 0, MODE_GESV = 1 };
@@ -43,5 +44,15 @@ hipError_t blocked_fused_getrf(int dtype, const Problem& p, hipStream_t s);
 bool blocked_supported(int dtype, int n);
 hipError_t blocked_getrf(int dtype, const Problem& p, hipStream_t s);
 hipError_t blocked_getrs(int dtype, const Problem& p, hipStream_t s);
+
+// Cholesky (potrf / potrs / posv), both triangles.  Register tier: n <= 64
+// (complex double 32), posv fused for nrhs <= 16.  Blocked tier: n <= 1024
+// (complex double 512).  Solve: n <= 1024.
+bool chol_register_supported(int dtype, int n);
+bool chol_blocked_supported(int dtype, int n);
+bool chol_solve_supported(int dtype, int n);
+hipError_t chol_register_launch(int dtype, const Problem& p, bool solve, hipStream_t s);
+hipError_t chol_blocked_launch(int dtype, const Problem& p, hipStream_t s);
+hipError_t chol_solve_launch(int dtype, const Problem& p, hipStream_t s);
 
 }  // namespace batchlu

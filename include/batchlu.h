@@ -140,6 +140,57 @@ int batchlu_getri(batchlu_dtype t, int n, const void* A, int lda,
                   hipStream_t stream);
 
 /*
+ * batchlu_potrf -- Cholesky factorisation of `batch` Hermitian (real:
+ * symmetric) positive definite n x n matrices, in place.
+ *   1 t, 2 uplo: 'L' computes A = L L^H and overwrites the lower triangle
+ *     with L; 'U' computes A = U^H U and overwrites the upper triangle with
+ *     U.  The other triangle is neither read nor written, and the imaginary
+ *     part of a diagonal entry is never read (a stored diagonal entry of the
+ *     factor has imaginary part +0),
+ *   3 n >= 0, 4 A (device), 5 lda >= max(1, n), 6 strideA >= lda*n when
+ *     batch > 1, 7 info (device int32[batch], out), 8 batch >= 0, 9 stream.
+ * info[b] = 0 on success, or j + 1 when column j is the first whose diagonal
+ * value (a_jj minus the squares of the row's earlier entries) is not
+ * positive or is NaN: then a_jj holds that value, the factorisation stops,
+ * and only columns 0 .. j-1 and a_jj of the factor are defined.  Orders up
+ * to 1024 (complex double 512); larger ones return BATCHLU_ERR_CAPACITY.
+ * Follows: BatchLAS "Blackwell" page, potrf rows of the status table and
+ * the LPanel paragraph (entries accumulate over k in ascending order), and
+ * the note that reference potf2 multiplies by a reciprocal of the diagonal.
+ */
+int batchlu_potrf(batchlu_dtype t, char uplo, int n, void* A, int lda,
+                  long long strideA, int* info, int batch, hipStream_t stream);
+
+/*
+ * batchlu_potrs -- solve A X = B with the factor of batchlu_potrf.
+ *   1 t, 2 uplo (the triangle holding the factor), 3 n, 4 nrhs >= 0,
+ *   5 A (device, read only), 6 lda, 7 strideA, 8 B (device, in: right-hand
+ *   sides, out: X), 9 ldb >= max(1, n), 10 strideB >= ldb*nrhs when
+ *   batch > 1, 11 batch, 12 stream.
+ * Forward with L (y_k = b_k / l_kk), then back with L^H, each a true
+ * division by the real diagonal as reference trsm does.  n <= 1024, else
+ * BATCHLU_ERR_CAPACITY.  Follows: BatchLAS "trsm" page, posv passages (posv
+ * is potrf followed by the two triangular solves).
+ */
+int batchlu_potrs(batchlu_dtype t, char uplo, int n, int nrhs, const void* A,
+                  int lda, long long strideA, void* B, int ldb,
+                  long long strideB, int batch, hipStream_t stream);
+
+/*
+ * batchlu_posv -- potrf on A, then potrs on B.
+ *   1 t, 2 uplo, 3 n, 4 nrhs, 5 A, 6 lda, 7 strideA, 8 B, 9 ldb,
+ *  10 strideB, 11 info, 12 batch, 13 stream.
+ * A matrix with info[b] > 0 keeps its B unchanged (LAPACK posv behaviour).
+ * For n <= 64 (complex double 32) and nrhs <= 16 the solve is fused into
+ * the factorisation kernel.  Follows: BatchLAS "Blackwell" page, posv
+ * passages (fused solve arm on both triangles) and "trsm" page, posv
+ * passages.
+ */
+int batchlu_posv(batchlu_dtype t, char uplo, int n, int nrhs, void* A,
+                 int lda, long long strideA, void* B, int ldb,
+                 long long strideB, int* info, int batch, hipStream_t stream);
+
+/*
  * batchlu_select_tier -- the tier an AUTO call would use for this shape
  * (op: 0 getrf, 1 getrs, 2 gesv), or BATCHLU_ERR_CAPACITY / -k on bad
  * arguments.  Host only, launches nothing.  Follows: BatchLAS "LU" page,

@@ -161,3 +161,20 @@ def spd_problem(seed: int, dtype, n: int, nrhs: int, batch: int):
     A = np.ascontiguousarray(np.swapaxes(M, 1, 2)).reshape(-1).astype(dt)   # column-major
     B = draw(rng, dt, batch * n * nrhs)
     return A, B
+
+
+# Cholesky shapes timed beside the LU workloads: the register-tier LU shape
+# (n = 32, eight right-hand sides), the work-group shape (complex n = 64,
+# sixteen right-hand sides) and the blocked double shape (n = 256, one
+# right-hand side), on Hermitian positive definite inputs (spd_problem).
+CHOL_WORKLOADS = {
+    "sposv_n32_r8_b32768": Workload("sposv_n32_r8_b32768", np.float32, 32, 8, 32768, "spd", "posv", 6),
+    "cposv_n64_r16_b8192": Workload("cposv_n64_r16_b8192", np.complex64, 64, 16, 8192, "spd", "posv", 7),
+    "dposv_n256_b1024": Workload("dposv_n256_b1024", np.float64, 256, 1, 1024, "spd", "posv", 8),
+}
+
+
+def chol_problem(w: Workload, batch: int | None = None):
+    """(A, B) of a Cholesky workload, flat, ld = n (both triangles stored)."""
+    b = w.batch if batch is None else min(batch, w.batch)
+    return spd_problem(w.seed, w.dtype, w.n, w.nrhs, b)
