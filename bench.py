@@ -5,7 +5,8 @@
 
 A step is one batched gesv (factor + forward + back substitution of every
 matrix of the batch; for the n = 1024 workload getrf then getrs) on synthetic
-inputs already resident in HBM.  The factorisation is in place, so every step
+inputs already resident in HBM; the Cholesky workloads time one batched posv
+(potrf + both triangular solves) the same way.  The factorisation is in place, so every step
 runs on its own pre-copied input set, and the sets rotate through enough
 bytes that they cannot all sit in the 256 MB last-level cache; copies happen
 outside the timed regions.
@@ -39,7 +40,8 @@ FP64_PEAK_TFLOPS = 78.6
 METRIC = "batched gesv matrices/s + GFLOP/s (n=32 f32, n=256 f64), % of roofline"
 HEADLINE = "sgesv_n32_r8_b32768"
 ORDER = ["sgesv_n16_b1024", "sgesv_n32_r8_b32768", "cgesv_n64_r16_b8192", "dgesv_n256_b1024",
-         "sgetrf_sgetrs_n1024_r32_b64"]
+         "sgetrf_sgetrs_n1024_r32_b64", "sposv_n32_r8_b32768", "cposv_n64_r16_b8192", "dposv_n256_b1024"]
+ALL_WORKLOADS = {**lu_inputs.WORKLOADS, **lu_inputs.CHOL_WORKLOADS}
 ROTATE_BYTES = 320 << 20          # in-place input bytes the rotating sets span at least
 MAX_SETS = 600
 # sources of the kernel whose HBM counters a workload's summary records
@@ -51,23 +53,36 @@ KERNEL_SOURCES = {
     "cgesv_n64_r16_b8192": [_C + "register_lu_kernel.h", _C + "device_ops.h"],
     "dgesv_n256_b1024": [_C + "blocked_fused.hip", _C + "device_ops.h"],
     "sgetrf_sgetrs_n1024_r32_b64": [_C + "blocked_lu_impl.h", _C + "device_ops.h"],
+    "sposv_n32_r8_b32768": [_C + "chol_kernels.h"],
+    "cposv_n64_r16_b8192": [_C + "chol_kernels.h"],
+    "dposv_n256_b1024": [_C + "chol_kernels.h"],
 }
 
 
+def is_chol(w) -> bool:
+    return w.op == "posv"
+
+
 def algorithmic_bytes(w) -> int:
-    """A read and written, B read and X written, ipiv and info written."""
+    """LU: A read and written, B read and X written, ipiv and info written.
+    Cholesky: the named triangle (n(n+1)/2 entries) read and written, B read
+    and X written, info written."""
     es = np.dtype(w.dtype).itemsize
+    if is_chol(w):
+        return es * (w.n * (w.n + 1) + 2 * w.n * w.nrhs) + 4
     return es * (2 * w.n * w.n + 2 * w.n * w.nrhs) + 4 * w.n + 4
 
 
 def algorithmic_flops(w) -> float:
-    """2/3 n^3 + 2 n^2 nrhs per matrix; complex counts 4 real flops per op."""
-    f = 2.0 / 3.0 * w.n ** 3 + 2.0 * w.n ** 2 * w.nrhs
+    """LU 2/3 n^3 + 2 n^2 nrhs, Cholesky 1/3 n^3 + 2 n^2 nrhs per matrix;
+    complex counts 4 real flops per operation."""
+    f = (1.0 if is_chol(w) else 2.0) / 3.0 * w.n ** 3 + 2.0 * w.n ** 2 * w.nrhs
     return f * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0)
 
 
 def getrf_flops(w) -> float:
-    return 2.0 / 3.0 * w.n ** 3 * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0)
+    """Flops of the factorisation alone (getrf 2/3 n^3, potrf 1/3 n^3)."""
+    return (1.0 if is_chol(w) else 2.0) / 3.0 * w.n ** 3 * (4.0 if np.dtype(w.dtype).kind == "c" else 1.0)
 
 
 def source_hash(workload: str) -> str:
@@ -224,7 +239,9 @@ def _oracle_step(w, A, B, m, nthreads):
     a = A[: m * n * n].copy()
     b = B[: m * n * r].copy()
     t0 = time.perf_counter()
-    if w.op == "gesv":
+    if is_chol(w):
+        _, used = oracle.posv(a, n, n, n * n, b, r, n, n * r, m, nthreads=nthreads)
+    elif w.op == "gesv":
         _, _, _, used = oracle.gesv(a, n, n, n * n, b, r, n, n * r, m, nthreads=nthreads)
     else:
         ipiv, _, _, used = oracle.getrf(a, n, n, n * n, m, nthreads=nthreads)
@@ -265,7 +282,7 @@ class Runner:
     def __init__(self, lib, torch, w, nsets):
         self.lib, self.torch, self.w = lib, torch, w
         dev = torch.device("cuda:0")
-        A, B = lu_inputs.dense_problem(w)
+        A, B = lu_inputs.chol_problem(w) if is_chol(w) else lu_inputs.dense_problem(w)
         self.hA, self.hB = A, B
         self.pA = torch.from_numpy(A).to(dev)
         self.pB = torch.from_numpy(B).to(dev)
@@ -286,7 +303,9 @@ class Runner:
         w, lib, t = self.w, self.lib, self.t
         dA, dB = self.sets[i % len(self.sets)]
         n, r = w.n, w.nrhs
-        if w.op == "gesv":
+        if is_chol(w):
+            lib.batchlu_posv(t, "L", n, r, dA, n, n * n, dB, n, n * r, self.info, w.batch, stream=self.stream)
+        elif w.op == "gesv":
             lib.batchlu_gesv(t, n, r, dA, n, n * n, self.ipiv, n, dB, n, n * r, self.info, w.batch,
                              stream=self.stream)
         else:
@@ -339,8 +358,12 @@ def parity_sample(r, k):
     n = w.n
     a0 = r.hA[: k * n * n].copy()
     b0 = r.hB[: k * n * w.nrhs].copy()
-    oracle.gesv(a0, n, n, n * n, b0, w.nrhs, n, n * w.nrhs, k)
     gA0 = r.sets[0][0][: k * n * n].cpu().numpy()
+    if is_chol(w):
+        oracle.posv(a0, n, n, n * n, b0, w.nrhs, n, n * w.nrhs, k)
+        return {"sampled_matrices": k, "factor_bitwise_equal": bool(np.array_equal(gA0.view(np.uint8),
+                                                                                   a0.view(np.uint8)))}
+    oracle.gesv(a0, n, n, n * n, b0, w.nrhs, n, n * w.nrhs, k)
     return {"sampled_matrices": k, "lu_bitwise_equal": bool(np.array_equal(gA0.view(np.uint8), a0.view(np.uint8)))}
 
 
@@ -349,7 +372,8 @@ def measure(lib, torch, w, steps, warmup, cpu_s, with_cpu):
     reps = max(7, steps)
     nsets = nsets_for(w, max(reps, warmup + steps))
     r = Runner(lib, torch, w, nsets)
-    tier = lib.batchlu_select_tier(r.t, 2 if w.op == "gesv" else 0, w.n, w.nrhs, w.batch)
+    op = 4 if is_chol(w) else (2 if w.op == "gesv" else 0)
+    tier = lib.batchlu_select_tier(r.t, op, w.n, w.nrhs, w.batch)
     for i in range(warmup):
         r.step(i)
     torch.cuda.synchronize()
@@ -381,16 +405,20 @@ def measure(lib, torch, w, steps, warmup, cpu_s, with_cpu):
         peak = FP64_PEAK_TFLOPS if np.dtype(w.dtype) in (np.float64, np.complex128) else FP32_MFMA_PEAK_TFLOPS
         n = w.n
         r.restore()
-        g = r.timed_each(lambda i: lib.batchlu_getrf(r.t, n, r.sets[i % nsets][0], n, n * n, r.ipiv, n, r.info,
-                                                     w.batch, stream=r.stream), reps)
+        if is_chol(w):
+            g = r.timed_each(lambda i: lib.batchlu_potrf(r.t, "L", n, r.sets[i % nsets][0], n, n * n, r.info,
+                                                         w.batch, stream=r.stream), reps)
+        else:
+            g = r.timed_each(lambda i: lib.batchlu_getrf(r.t, n, r.sets[i % nsets][0], n, n * n, r.ipiv, n, r.info,
+                                                         w.batch, stream=r.stream), reps)
         gmed, gmean = float(np.median(g)), float(np.mean(g))
         fl = getrf_flops(w) * w.batch
         tf = fl / (gmean * 1e-3) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
                            "traffic": traffic_from_profile(w.name), "kernel_ms_mean": gmean,
                            "kernel_ms_median": gmed, "algorithmic_flops_per_launch": fl,
-                           "scope": "batchlu_getrf (every launch it makes)"}
-        if w.op != "gesv":
+                           "scope": ("batchlu_potrf" if is_chol(w) else "batchlu_getrf") + " (every launch it makes)"}
+        if w.op == "getrf+getrs":
             # the solve and the inverse on the factors of the last getrf
             es = np.dtype(w.dtype).itemsize
             dA = r.sets[(reps - 1) % nsets][0].clone()   # the factors that r.ipiv belongs to
@@ -425,7 +453,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="all", choices=["all"] + sorted(lu_inputs.WORKLOADS))
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(ALL_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-run-s", type=float, default=0.4, help="least wall time of one timed oracle run")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -480,10 +508,10 @@ def main():
     results = {}
     for name in names:
         print(f"# {name}", file=sys.stderr, flush=True)
-        results[name] = measure(lib, torch, lu_inputs.WORKLOADS[name], args.steps, args.warmup, args.cpu_run_s,
+        results[name] = measure(lib, torch, ALL_WORKLOADS[name], args.steps, args.warmup, args.cpu_run_s,
                                 not args.no_cpu_baseline)
     h = results[head]
-    w = lu_inputs.WORKLOADS[head]
+    w = ALL_WORKLOADS[head]
     ms_per_step = h["wall_ms_per_step"]
     line = {
         "metric": METRIC,

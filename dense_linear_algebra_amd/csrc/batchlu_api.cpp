@@ -306,10 +306,11 @@ int batchlu_posv(batchlu_dtype t, char uplo, int n, int nrhs, void* A, int lda, 
 
 int batchlu_select_tier(batchlu_dtype t, int op, int n, int nrhs, int batch) {
     if (!valid_dtype(t)) return -1;
-    if (op < OP_GETRF || op > OP_GESV) return -2;
+    if (op < OP_GETRF || op > 4) return -2;
     if (n < 0) return -3;
     if (nrhs < 0) return -4;
     if (batch < 0) return -5;
+    if (op >= 3) return chol_tier(t, n);   // 3 potrf, 4 posv
     return choose(t, op, n, nrhs);
 }
 

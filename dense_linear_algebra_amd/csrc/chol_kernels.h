@@ -8,11 +8,11 @@
 // redesigned for wave64:
 //   register   n <= 64 (complex double: 32): NB lanes of a wavefront hold one
 //              matrix, lane i its row i of the lower factor in VGPRs.  Step
-//              j publishes column j (unscaled) in LDS; every lane forms the
-//              same r = 1/sqrt(d) and scales what it reads, so one wavefront
-//              sync per step carries the whole column.  posv rides along:
-//              the forward solve is fused into the elimination steps, the
-//              back solve publishes row k of L and x_k per step.
+//              j publishes column j in LDS; every lane forms the same
+//              r = 1/sqrt(d), scales its own entry and publishes it.  posv
+//              rides along: the forward solve is fused into the elimination
+//              steps, the back solve publishes row k of L per step, and the
+//              divisions by the diagonal are spread over the lanes.
 //   blocked    n <= 1024, nb = 32, right-looking: one work-group per matrix
 //              factors the (n - j0) x 32 panel with one row per thread and
 //              one barrier per column (double-buffered column slot); the
@@ -151,8 +151,11 @@ __global__ void __launch_bounds__(64 * kRegWaves) chol_reg_kernel(Problem p)
     constexpr int GPW = 64 / NB;                   // matrices per wavefront
     constexpr int GPB = GPW * kRegWaves;           // matrices per block
     constexpr int NRP = NR > 0 ? NR : 1;
+    constexpr int QPL = (NRP + NB - 1) / NB;       // right-hand sides divided per lane
     __shared__ T colbuf[GPB][NB];                  // column j (unscaled) / row k of L
-    __shared__ T ybuf[GPB][NRP];                   // y_j or x_k
+    __shared__ T lbuf[GPB][NB];                    // column j scaled: l_kj
+    __shared__ T ybuf[GPB][NRP];                   // b_j (or y_k) before its division
+    __shared__ T xbuf[GPB][NRP];                   // y_j (or x_k) after it
 
     const int lane = threadIdx.x & 63;
     const int grp = (threadIdx.x >> 6) * GPW + lane / NB;
@@ -180,11 +183,23 @@ __global__ void __launch_bounds__(64 * kRegWaves) chol_reg_kernel(Problem p)
 
     int info = 0;
     T* col = &colbuf[grp][0];
+    T* lcol = &lbuf[grp][0];
     T* yb = &ybuf[grp][0];
+    T* xb = &xbuf[grp][0];
+    // Step j: lanes at or below the diagonal publish column j unscaled (and
+    // lane j its right-hand-side row); every lane forms the same l_jj and
+    // r = 1/l_jj; each lane scales its own entry and publishes it, and the
+    // divisions y_j = b_j / l_jj are spread over the group's lanes; then the
+    // rows below update with the scaled column and y_j.
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         if (j >= n) continue;   // uniform; a guard, not a break, keeps the loop unrolled
         if (li >= j) col[li] = a[j];
+        if constexpr (NR > 0) {
+            if (li == j)
+#pragma unroll
+                for (int q = 0; q < NR; ++q) yb[q] = b[q];
+        }
         wave_sync();
         const R d = O::re(col[j]);
         const bool ok = d > R(0);
@@ -192,47 +207,60 @@ __global__ void __launch_bounds__(64 * kRegWaves) chol_reg_kernel(Problem p)
         const R ljj = sqrt_r(d);
         const R r = R(1) / ljj;
         if (li == j) a[j] = O::diag(ok ? ljj : d);
-        else if (li > j) a[j] = O::scale(a[j], r);
+        else if (li > j) {
+            a[j] = O::scale(a[j], r);
+            lcol[li] = a[j];
+        }
         if constexpr (NR > 0) {
-            if (li == j) {
 #pragma unroll
-                for (int q = 0; q < NR; ++q) {
-                    b[q] = O::divr(b[q], ljj);
-                    yb[q] = b[q];
-                }
+            for (int t = 0; t < QPL; ++t) {
+                const int q = li + NB * t;
+                if (q < NR) xb[q] = O::divr(yb[q], ljj);
             }
         }
         wave_sync();
         if (li > j) {
 #pragma unroll
-            for (int k = j + 1; k < NB; ++k) O::fms_conj(a[k], a[j], O::scale(col[k], r));
+            for (int k = j + 1; k < NB; ++k) O::fms_conj(a[k], a[j], lcol[k]);
             if constexpr (NR > 0) {
 #pragma unroll
-                for (int q = 0; q < NR; ++q) O::fms(b[q], a[j], yb[q]);
+                for (int q = 0; q < NR; ++q) O::fms(b[q], a[j], xb[q]);
             }
+        } else if constexpr (NR > 0) {
+            if (li == j)
+#pragma unroll
+                for (int q = 0; q < NR; ++q) b[q] = xb[q];
         }
         wave_sync();
     }
 
-    // back solve with L^H: x_k = y_k / l_kk, then y_i -= conj(l_ki) x_k
+    // back solve with L^H: x_k = y_k / l_kk (spread over the lanes), then
+    // y_i -= conj(l_ki) x_k for the rows above
     if constexpr (NR > 0) {
 #pragma unroll
         for (int k = NB - 1; k >= 0; --k) {
             if (k >= n) continue;
             if (li == k) {
 #pragma unroll
-                for (int q = 0; q < NR; ++q) {
-                    b[q] = O::divr(b[q], O::re(a[k]));
-                    yb[q] = b[q];
-                }
+                for (int q = 0; q < NR; ++q) yb[q] = b[q];
 #pragma unroll
-                for (int c = 0; c < k; ++c) col[c] = a[c];
+                for (int c = 0; c <= k; ++c) col[c] = a[c];
+            }
+            wave_sync();
+            const R lkk = O::re(col[k]);
+#pragma unroll
+            for (int t = 0; t < QPL; ++t) {
+                const int q = li + NB * t;
+                if (q < NR) xb[q] = O::divr(yb[q], lkk);
             }
             wave_sync();
             if (li < k) {
                 const T lki = col[li];
 #pragma unroll
-                for (int q = 0; q < NR; ++q) O::fms_cx(b[q], lki, yb[q]);
+                for (int q = 0; q < NR; ++q) O::fms_cx(b[q], lki, xb[q]);
+            } else if (li == k) {
+#pragma unroll
+                for (int q = 0; q < NR; ++q) b[q] = xb[q];
             }
             wave_sync();
         }

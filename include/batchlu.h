@@ -192,7 +192,8 @@ int batchlu_posv(batchlu_dtype t, char uplo, int n, int nrhs, void* A,
 
 /*
  * batchlu_select_tier -- the tier an AUTO call would use for this shape
- * (op: 0 getrf, 1 getrs, 2 gesv), or BATCHLU_ERR_CAPACITY / -k on bad
+ * (op: 0 getrf, 1 getrs, 2 gesv, 3 potrf, 4 posv; the Cholesky register
+ * kernel reports as BATCHLU_TIER_CTA), or BATCHLU_ERR_CAPACITY / -k on bad
  * arguments.  Host only, launches nothing.  Follows: BatchLAS "LU" page,
  * routing tables (a rank of tiers per shape).
  */
