@@ -21,7 +21,8 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "lu_oracle.c"), os.path.join(_HERE, "chol_oracle.c")]
+_SRCS = [os.path.join(_HERE, "lu_oracle.c"), os.path.join(_HERE, "chol_oracle.c"),
+         os.path.join(_HERE, "lu_rect_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +64,8 @@ def _load():
             lib.oracle_gesv_batch.restype = i32
             lib.oracle_chol_batch.argtypes = [i32, i32, i32, i32, i32, vp, i32, i64, ip, vp, i32, i64, i32, i32]
             lib.oracle_chol_batch.restype = i32
+            lib.oracle_getrf_rect_batch.argtypes = [i32, i32, i32, vp, i32, i64, ip, i64, ip, dp, i32, i32]
+            lib.oracle_getrf_rect_batch.restype = i32
             _lib = lib
     return _lib
 
@@ -142,6 +145,22 @@ def gesv(A, n, lda, strideA, B, nrhs, ldb, strideB, batch, want_margins=False, n
     used = _load().oracle_gesv_batch(_code(A), n, nrhs, _ptr(A), lda, strideA, _ptr(ipiv), n, _ptr(B), ldb,
                                      strideB, _ptr(info), _ptr(margins), batch, nthreads)
     return ipiv[:, :max(n, 0)], info, margins, used
+
+
+def getrf_rect(A, m, n, lda, strideA, batch, strideP=None, want_margins=False, nthreads=0):
+    """LU with partial pivoting of ``batch`` m x n matrices in place (min(m, n)
+    steps).  Returns ``(ipiv (batch, strideP), info, margins, threads_used)``;
+    ipiv holds min(m, n) 1-based entries per matrix."""
+    k = min(m, n)
+    strideP = max(k, 1) if strideP is None else strideP
+    if batch > 0 and m > 0 and n > 0:
+        _check_flat(A, (batch - 1) * strideA + (n - 1) * lda + m, "A")
+    ipiv = np.zeros((max(batch, 0), max(strideP, 1)), np.int32)
+    info = np.zeros(max(batch, 0), np.int32)
+    margins = np.zeros((max(batch, 0), max(k, 1)), np.float64) if want_margins else None
+    used = _load().oracle_getrf_rect_batch(_code(A), m, n, _ptr(A), lda, strideA, _ptr(ipiv), ipiv.shape[1],
+                                           _ptr(info), _ptr(margins), batch, nthreads)
+    return ipiv[:, :k], info, margins, used
 
 
 def _uplo(uplo):
@@ -286,4 +305,24 @@ def chol_residual(A, F, uplo="L"):
     L = _wide(chol_factor(F, uplo))
     num = np.sqrt(np.sum(np.abs(H - L @ L.conj().T) ** 2))
     den = n * eps_of(A.dtype) * np.sqrt(np.sum(np.abs(H) ** 2))
+    return float(num / den) if den > 0 else float(num)
+
+
+def rect_residual(A, LU, ipiv):
+    """||P A - L U||_F / (max(m, n) eps ||A||_F) for an m x n factorisation
+    (L m x k unit lower trapezoidal, U k x n upper trapezoidal, k = min(m, n))."""
+    m, n = A.shape
+    k = min(m, n)
+    if k == 0:
+        return 0.0
+    W = _wide(LU)
+    L = np.tril(W[:, :k], -1) + np.eye(m, k, dtype=W.dtype)
+    U = np.triu(W[:k, :])
+    perm = np.arange(m)
+    for j in range(k):
+        p = int(ipiv[j]) - 1
+        perm[j], perm[p] = perm[p], perm[j]
+    PA = _wide(A)[perm]
+    num = np.sqrt(np.sum(np.abs(PA - L @ U) ** 2))
+    den = max(m, n) * eps_of(A.dtype) * np.sqrt(np.sum(np.abs(_wide(A)) ** 2))
     return float(num / den) if den > 0 else float(num)
