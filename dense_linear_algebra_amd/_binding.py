@@ -43,6 +43,10 @@ def load():
     lib.batchlu_gesv.argtypes = [i32, i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, vp, i32, vp]
     lib.batchlu_getri.argtypes = [i32, i32, vp, i32, i64, vp, i64, vp, i32, i64, i32, vp]
     lib.batchlu_potrf.argtypes = [i32, ch, i32, vp, i32, i64, vp, i32, vp]
+    lib.batchlu_getrf_rect.argtypes = [i32, i32, i32, vp, i32, i64, vp, i64, vp, i32, vp]
+    lib.batchlu_getrf_vbatched.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.batchlu_getrs_vbatched.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+    lib.batchlu_gesv_vbatched.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     lib.batchlu_potrs.argtypes = [i32, ch, i32, i32, vp, i32, i64, vp, i32, i64, i32, vp]
     lib.batchlu_posv.argtypes = [i32, ch, i32, i32, vp, i32, i64, vp, i32, i64, vp, i32, vp]
     lib.batchlu_check_reciprocal.argtypes = [ctypes.c_uint, ctypes.c_uint, vp, vp, vp]
@@ -54,7 +58,8 @@ def load():
     lib.batchlu_version.argtypes = []
     lib.batchlu_version.restype = ctypes.c_char_p
     for f in ("batchlu_getrf", "batchlu_getrs", "batchlu_gesv", "batchlu_getri", "batchlu_potrf", "batchlu_potrs",
-              "batchlu_posv", "batchlu_select_tier", "batchlu_set_tier"):
+              "batchlu_posv", "batchlu_getrf_rect", "batchlu_getrf_vbatched", "batchlu_getrs_vbatched",
+              "batchlu_gesv_vbatched", "batchlu_select_tier", "batchlu_set_tier"):
         getattr(lib, f).restype = i32
     _lib = lib
     return lib
@@ -122,6 +127,32 @@ def batchlu_gesv(t, n, nrhs, A, lda, strideA, ipiv, strideP, B, ldb, strideB, in
     st = load().batchlu_gesv(t, n, nrhs, _ptr(A), lda, strideA, _ptr(ipiv), strideP, _ptr(B), ldb, strideB,
                              _ptr(info), batch, _stream(stream))
     return _check("batchlu_gesv", st, raise_on_error)
+
+
+def batchlu_getrf_rect(t, m, n, A, lda, strideA, ipiv, strideP, info, batch, stream=None, raise_on_error=True):
+    st = load().batchlu_getrf_rect(t, m, n, _ptr(A), lda, strideA, _ptr(ipiv), strideP, _ptr(info), batch,
+                                   _stream(stream))
+    return _check("batchlu_getrf_rect", st, raise_on_error)
+
+
+def batchlu_getrf_vbatched(t, m, n, A, lda, ipiv, info, max_m, max_n, batch, stream=None, raise_on_error=True):
+    """m, n, lda, info: device int32 arrays; A, ipiv: device arrays of device
+    pointers (int64 tensors holding the addresses)."""
+    st = load().batchlu_getrf_vbatched(t, _ptr(m), _ptr(n), _ptr(A), _ptr(lda), _ptr(ipiv), _ptr(info), max_m,
+                                       max_n, batch, _stream(stream))
+    return _check("batchlu_getrf_vbatched", st, raise_on_error)
+
+
+def batchlu_getrs_vbatched(t, n, nrhs, A, lda, ipiv, B, ldb, max_n, batch, stream=None, raise_on_error=True):
+    st = load().batchlu_getrs_vbatched(t, _ptr(n), _ptr(nrhs), _ptr(A), _ptr(lda), _ptr(ipiv), _ptr(B), _ptr(ldb),
+                                       max_n, batch, _stream(stream))
+    return _check("batchlu_getrs_vbatched", st, raise_on_error)
+
+
+def batchlu_gesv_vbatched(t, n, nrhs, A, lda, ipiv, B, ldb, info, max_n, batch, stream=None, raise_on_error=True):
+    st = load().batchlu_gesv_vbatched(t, _ptr(n), _ptr(nrhs), _ptr(A), _ptr(lda), _ptr(ipiv), _ptr(B), _ptr(ldb),
+                                      _ptr(info), max_n, batch, _stream(stream))
+    return _check("batchlu_gesv_vbatched", st, raise_on_error)
 
 
 def _uplo(uplo):

@@ -304,6 +304,85 @@ int batchlu_posv(batchlu_dtype t, char uplo, int n, int nrhs, void* A, int lda, 
     return status_of(chol_solve_launch(t, p, stream));   // skips matrices whose info > 0
 }
 
+// ---------------------------------------------------------------------------
+// Rectangular and variable-size LU (one work-group per matrix).
+// ---------------------------------------------------------------------------
+int batchlu_getrf_rect(batchlu_dtype t, int m, int n, void* A, int lda, long long strideA, int* ipiv,
+                       long long strideP, int* info, int batch, hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (m < 0) return -2;
+    if (n < 0) return -3;
+    if (lda < (m > 1 ? m : 1)) return -5;
+    if (batch < 0) return -10;
+    const int k = m < n ? m : n;
+    if (batch > 1 && strideA < (long long)lda * n) return -6;
+    if (batch > 1 && strideP < k) return -8;
+    if (m == 0 || n == 0 || batch == 0) return BATCHLU_OK;   // no work: nothing is launched
+    if (!info) return -9;
+    if (!A) return -4;
+    if (!ipiv) return -7;
+    if (m == n) return batchlu_getrf(t, n, A, lda, strideA, ipiv, strideP, info, batch, stream);
+    if (m > general_max_rows(t) || n > 1024) return BATCHLU_ERR_CAPACITY;
+    return status_of(general_getrf_strided(t, A, m, n, lda, strideA, ipiv, strideP, info, batch, stream));
+}
+
+int batchlu_getrf_vbatched(batchlu_dtype t, const int* m, const int* n, void* const* A, const int* lda,
+                           int* const* ipiv, int* info, int max_m, int max_n, int batch, hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (batch < 0) return -10;
+    if (max_m < 0) return -8;
+    if (max_n < 0) return -9;
+    if (batch == 0) return BATCHLU_OK;
+    if (!m) return -2;
+    if (!n) return -3;
+    if (!A) return -4;
+    if (!lda) return -5;
+    if (!ipiv) return -6;
+    if (!info) return -7;
+    if (max_m > general_max_rows(t) || max_n > 1024) return BATCHLU_ERR_CAPACITY;
+    return status_of(general_getrf_vbatched(t, A, m, n, lda, ipiv, info, max_m > 0 ? max_m : 1, batch, stream));
+}
+
+int batchlu_getrs_vbatched(batchlu_dtype t, const int* n, const int* nrhs, void* const* A, const int* lda,
+                           int* const* ipiv, void* const* B, const int* ldb, int max_n, int batch,
+                           hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (max_n < 0) return -9;
+    if (batch < 0) return -10;
+    if (batch == 0 || max_n == 0) return BATCHLU_OK;
+    if (!n) return -2;
+    if (!nrhs) return -3;
+    if (!A) return -4;
+    if (!lda) return -5;
+    if (!ipiv) return -6;
+    if (!B) return -7;
+    if (!ldb) return -8;
+    if (max_n > 1024) return BATCHLU_ERR_CAPACITY;
+    return status_of(general_getrs_vbatched(t, A, n, lda, ipiv, nrhs, B, ldb, nullptr, max_n, batch, stream));
+}
+
+int batchlu_gesv_vbatched(batchlu_dtype t, const int* n, const int* nrhs, void* const* A, const int* lda,
+                          int* const* ipiv, void* const* B, const int* ldb, int* info, int max_n, int batch,
+                          hipStream_t stream) {
+    if (!valid_dtype(t)) return -1;
+    if (max_n < 0) return -10;
+    if (batch < 0) return -11;
+    if (batch == 0) return BATCHLU_OK;
+    if (!n) return -2;
+    if (!nrhs) return -3;
+    if (!A) return -4;
+    if (!lda) return -5;
+    if (!ipiv) return -6;
+    if (!B) return -7;
+    if (!ldb) return -8;
+    if (!info) return -9;
+    if (max_n > general_max_rows(t) || max_n > 1024) return BATCHLU_ERR_CAPACITY;
+    const int mm = max_n > 0 ? max_n : 1;
+    int st = status_of(general_getrf_vbatched(t, A, n, n, lda, ipiv, info, mm, batch, stream));
+    if (st != BATCHLU_OK) return st;
+    return status_of(general_getrs_vbatched(t, A, n, lda, ipiv, nrhs, B, ldb, info, mm, batch, stream));
+}
+
 int batchlu_select_tier(batchlu_dtype t, int op, int n, int nrhs, int batch) {
     if (!valid_dtype(t)) return -1;
     if (op < OP_GETRF || op > 4) return -2;

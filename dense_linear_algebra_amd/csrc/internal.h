@@ -48,6 +48,19 @@ hipError_t blocked_getrs(int dtype, const Problem& p, hipStream_t s);
 // Cholesky (potrf / potrs / posv), both triangles.  Register tier: n <= 64
 // (complex double 32), posv fused for nrhs <= 16.  Blocked tier: n <= 1024
 // (complex double 512).  Solve: n <= 1024.
+// LU of m x n matrices and of variable-size batches (one work-group per
+// matrix, m <= general_max_rows, n <= 1024); the solve for square
+// variable-size batches (n <= 1024).  Matrices whose sizes fall outside
+// what the launch covers get info = -1 and are not touched.
+int general_max_rows(int dtype);
+hipError_t general_getrf_strided(int dtype, void* A, int m, int n, int lda, long long sA, int* ipiv, long long sP,
+                                 int* info, int batch, hipStream_t s);
+hipError_t general_getrf_vbatched(int dtype, void* const* A, const int* m, const int* n, const int* lda,
+                                  int* const* ipiv, int* info, int max_m, int batch, hipStream_t s);
+hipError_t general_getrs_vbatched(int dtype, void* const* A, const int* n, const int* lda, int* const* ipiv,
+                                  const int* nrhs, void* const* B, const int* ldb, int* info, int max_n, int batch,
+                                  hipStream_t s);
+
 bool chol_register_supported(int dtype, int n);
 bool chol_blocked_supported(int dtype, int n);
 bool chol_solve_supported(int dtype, int n);

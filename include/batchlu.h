@@ -140,6 +140,73 @@ int batchlu_getri(batchlu_dtype t, int n, const void* A, int lda,
                   hipStream_t stream);
 
 /*
+ * batchlu_getrf_rect -- LU with partial pivoting of `batch` m x n matrices
+ * (LAPACK getrf on a rectangular A), in place: min(m, n) steps, each
+ * searching all m rows of its column, swapping whole rows and updating every
+ * column to its right.
+ *   1 t, 2 m >= 0, 3 n >= 0, 4 A (device), 5 lda >= max(1, m),
+ *   6 strideA >= lda*n when batch > 1, 7 ipiv (device int32, min(m, n)
+ *   1-based entries per matrix), 8 strideP >= min(m, n) when batch > 1,
+ *   9 info (device int32[batch]: 0, or the first step whose pivot is exactly
+ *   zero, 1-based), 10 batch, 11 stream.
+ * m == n runs batchlu_getrf.  Otherwise m <= 1024 for float (512 for double
+ * and complex float, 256 for complex double) and n <= 1024, else
+ * BATCHLU_ERR_CAPACITY.  Pivot, tie, NaN, zero-pivot and
+ * rounding conventions are those of batchlu_getrf.  m == 0, n == 0 or
+ * batch == 0 launch nothing.  Follows: BatchLAS "LU" page, family table (a
+ * non-square A is served there only by the vendor's LAPACK-style getrf).
+ */
+int batchlu_getrf_rect(batchlu_dtype t, int m, int n, void* A, int lda,
+                       long long strideA, int* ipiv, long long strideP,
+                       int* info, int batch, hipStream_t stream);
+
+/*
+ * batchlu_getrf_vbatched -- LU with partial pivoting of a batch whose
+ * matrices differ in size: matrix b is m[b] x n[b] at A[b] with leading
+ * dimension lda[b] and pivots ipiv[b] (min(m[b], n[b]) entries).
+ *   1 t, 2 m, 3 n, 5 lda (device int32[batch] each), 4 A (device array of
+ *   batch device pointers), 6 ipiv (device array of batch device int32
+ *   pointers), 7 info (device int32[batch], out), 8 max_m, 9 max_n (upper
+ *   bounds of m[b] and n[b]: max_m within the rows batchlu_getrf_rect
+ *   takes for the type, max_n <= 1024, else BATCHLU_ERR_CAPACITY), 10 batch, 11 stream.
+ * A matrix whose sizes are negative, above max_m / max_n, or whose
+ * lda[b] < max(1, m[b]), is not touched and gets info[b] = -1.  One launch
+ * for the whole batch (one work-group per matrix).  Follows: BatchLAS "LU"
+ * page, family table (a heterogeneous A has no route there).
+ */
+int batchlu_getrf_vbatched(batchlu_dtype t, const int* m, const int* n,
+                           void* const* A, const int* lda, int* const* ipiv,
+                           int* info, int max_m, int max_n, int batch,
+                           hipStream_t stream);
+
+/*
+ * batchlu_getrs_vbatched -- solve A_b X_b = B_b (NoTrans) for a square
+ * variable-size batch with the factors and pivots of batchlu_getrf_vbatched.
+ *   1 t, 2 n, 3 nrhs, 5 lda, 8 ldb (device int32[batch] each), 4 A, 7 B
+ *   (device arrays of batch device pointers; B[b] is n[b] x nrhs[b], in:
+ *   right-hand sides, out: X), 6 ipiv (device array of pointers),
+ *   9 max_n (upper bound of n[b], <= 1024), 10 batch, 11 stream.
+ * Matrices with n[b] <= 0, nrhs[b] <= 0, n[b] above max_n rounded up to 64,
+ * or lda[b] / ldb[b] < n[b] are skipped.  Order of operations as
+ * batchlu_getrs.
+ */
+int batchlu_getrs_vbatched(batchlu_dtype t, const int* n, const int* nrhs,
+                           void* const* A, const int* lda, int* const* ipiv,
+                           void* const* B, const int* ldb, int max_n,
+                           int batch, hipStream_t stream);
+
+/*
+ * batchlu_gesv_vbatched -- batchlu_getrf_vbatched (square, m = n), then
+ * batchlu_getrs_vbatched on the matrices whose info is 0 (the others keep
+ * their B).  Arguments as those two; 9 info (device int32[batch], out),
+ * 10 max_n, 11 batch, 12 stream.
+ */
+int batchlu_gesv_vbatched(batchlu_dtype t, const int* n, const int* nrhs,
+                          void* const* A, const int* lda, int* const* ipiv,
+                          void* const* B, const int* ldb, int* info,
+                          int max_n, int batch, hipStream_t stream);
+
+/*
  * batchlu_potrf -- Cholesky factorisation of `batch` Hermitian (real:
  * symmetric) positive definite n x n matrices, in place.
  *   1 t, 2 uplo: 'L' computes A = L L^H and overwrites the lower triangle
