@@ -40,8 +40,10 @@ FP64_PEAK_TFLOPS = 78.6
 METRIC = "batched gesv matrices/s + GFLOP/s (n=32 f32, n=256 f64), % of roofline"
 HEADLINE = "sgesv_n32_r8_b32768"
 ORDER = ["sgesv_n16_b1024", "sgesv_n32_r8_b32768", "cgesv_n64_r16_b8192", "dgesv_n256_b1024",
-         "sgetrf_sgetrs_n1024_r32_b64", "sposv_n32_r8_b32768", "cposv_n64_r16_b8192", "dposv_n256_b1024"]
-ALL_WORKLOADS = {**lu_inputs.WORKLOADS, **lu_inputs.CHOL_WORKLOADS}
+         "sgetrf_sgetrs_n1024_r32_b64", "sposv_n32_r8_b32768", "cposv_n64_r16_b8192", "dposv_n256_b1024",
+         "sgetrf_m512_n128_b2048", "sgesv_vbatched_n16_256_r1_b4096"]
+ALL_WORKLOADS = {**lu_inputs.WORKLOADS, **lu_inputs.CHOL_WORKLOADS, **lu_inputs.RECT_WORKLOADS,
+                 **lu_inputs.VBATCH_WORKLOADS}
 ROTATE_BYTES = 320 << 20          # in-place input bytes the rotating sets span at least
 MAX_SETS = 600
 # sources of the kernel whose HBM counters a workload's summary records
@@ -448,6 +450,171 @@ def measure(lib, torch, w, steps, warmup, cpu_s, with_cpu):
     return out
 
 
+# ---------------------------------------------------------------------------
+# rectangular and variable-size LU (one work-group per matrix, VALU)
+# ---------------------------------------------------------------------------
+
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+
+def _timed(torch, fn, reps, stream):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        fn(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def rect_flops(m, n):
+    """m n^2 - n^3/3 (m >= n), else n m^2 - m^3/3, less the lower-order terms."""
+    k, big = min(m, n), max(m, n)
+    return big * k * k - k ** 3 / 3.0
+
+
+def measure_rect(lib, torch, w, steps, warmup, cpu_s, with_cpu):
+    import oracle
+    m, n = lu_inputs.RECT_ROWS[w.name], w.n
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    A = lu_inputs.draw(rng, w.dtype, w.batch * m * n)
+    es = np.dtype(w.dtype).itemsize
+    reps = max(7, steps)
+    nsets = int(min(MAX_SETS, max(reps + warmup, -(-ROTATE_BYTES // (es * m * n * w.batch)))))
+    dev = torch.device("cuda:0")
+    pA = torch.from_numpy(A).to(dev)
+    sets = [pA.clone() for _ in range(nsets)]
+    k = min(m, n)
+    ipiv = torch.empty(w.batch * k, dtype=torch.int32, device=dev)
+    info = torch.empty(w.batch, dtype=torch.int32, device=dev)
+    t = lib.dtype_code(A.dtype)
+    stream = torch.cuda.current_stream()
+    step = lambda i: lib.batchlu_getrf_rect(t, m, n, sets[i % nsets], m, m * n, ipiv, k, info, w.batch,  # noqa
+                                            stream=stream)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a0 = A[: 2 * m * n].copy()
+    oracle.getrf_rect(a0, m, n, m, m * n, 2)
+    parity = {"sampled_matrices": 2,
+              "lu_bitwise_equal": bool(np.array_equal(sets[0][: 2 * m * n].cpu().numpy().view(np.uint8),
+                                                      a0.view(np.uint8)))}
+    for s_ in sets:
+        s_.copy_(pA)
+    ms = _timed(torch, step, reps, stream)
+    med, mean = float(np.median(ms)), float(np.mean(ms))
+    fl = rect_flops(m, n) * w.batch
+    tf = fl / (mean * 1e-3) / 1e12
+    out = {"m": m, "n": n, "batch": w.batch, "dtype": np.dtype(w.dtype).name, "op": "getrf_rect",
+           "tier": "general", "input_sets": nsets, "step_ms_median": med, "step_ms_mean": mean, "reps": reps,
+           "matrices_per_s": w.batch / (med * 1e-3), "gflops": fl / (med * 1e-3) / 1e9, "parity": parity,
+           "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None, "kernel_ms_mean": mean,
+                        "kernel_ms_median": med, "algorithmic_flops_per_launch": fl,
+                        "scope": "batchlu_getrf_rect (one launch)"}}
+    if with_cpu:
+        def run(mm, nt):
+            a = A[: mm * m * n].copy()
+            t0 = time.perf_counter()
+            _, _, _, used = oracle.getrf_rect(a, m, n, m, m * n, mm, nthreads=nt)
+            return time.perf_counter() - t0, used
+        out["cpu_baseline"] = _bounded_oracle_rate(run, w.batch, cpu_s, "getrf_rect")
+    del sets, pA
+    torch.cuda.empty_cache()
+    return out
+
+
+def _bounded_oracle_rate(run, batch, cpu_s, what):
+    """Matrices/s of run(m, threads) on the first m matrices (m doubled until
+    one run takes cpu_s), median of 3, on all cores and on one."""
+    res = {}
+    for nt in (0, 1):
+        mm = 1 if nt == 1 else min(batch, os.cpu_count() or 1)
+        while True:
+            dt, used = run(mm, nt)
+            if dt >= cpu_s or mm >= batch:
+                break
+            mm = min(batch, mm * 2)
+        times = sorted([dt] + [run(mm, nt)[0] for _ in range(2)])
+        res[nt] = (mm / times[1], used, mm, times[1])
+    all_rate, used, m_all, t_all = res[0]
+    one_rate, _, m_one, t_one = res[1]
+    return {"value": all_rate, "unit": "matrices/s", "cores": used, "kind": "oracle",
+            "sample": f"median of 3 runs of the oracle's {what} on the first {m_all} matrices ({t_all:.2f} s each)",
+            "single_core": {"value": one_rate, "unit": "matrices/s", "cores": 1,
+                            "sample": f"median of 3 runs on the first {m_one} matrices ({t_one:.2f} s each)"}}
+
+
+def measure_vbatch(lib, torch, w, steps, warmup, cpu_s, with_cpu):
+    import oracle
+    orders, A, B, aoff, boff = lu_inputs.vbatch_problem(w)
+    es = np.dtype(w.dtype).itemsize
+    reps = max(7, steps)
+    per_set = es * (A.size + B.size)
+    nsets = int(min(MAX_SETS, max(reps + warmup, -(-ROTATE_BYTES // per_set))))
+    dev = torch.device("cuda:0")
+    pA, pB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    sets = [(pA.clone(), pB.clone()) for _ in range(nsets)]
+    dn = torch.from_numpy(orders).to(dev)
+    dr = torch.full((w.batch,), w.nrhs, dtype=torch.int32, device=dev)
+    maxn = int(orders.max())
+    dpiv = torch.empty(w.batch * maxn, dtype=torch.int32, device=dev)
+    pptr = torch.tensor(dpiv.data_ptr() + 4 * maxn * np.arange(w.batch, dtype=np.int64), device=dev)
+    info = torch.empty(w.batch, dtype=torch.int32, device=dev)
+    ptrs = [(torch.tensor(a.data_ptr() + es * aoff, device=dev), torch.tensor(b.data_ptr() + es * boff, device=dev))
+            for a, b in sets]
+    t = lib.dtype_code(A.dtype)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        pa, pb = ptrs[i % nsets]
+        lib.batchlu_gesv_vbatched(t, dn, dr, pa, dn, pptr, pb, dn, info, maxn, w.batch, stream=stream)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    gA, gB = sets[0][0].cpu().numpy(), sets[0][1].cpu().numpy()
+    ok = True
+    for b in (0, w.batch // 2, w.batch - 1):
+        nb_, sa, sb = int(orders[b]), int(aoff[b]), int(boff[b])
+        a, bb = A[sa: sa + nb_ * nb_].copy(), B[sb: sb + nb_ * w.nrhs].copy()
+        oracle.gesv(a, nb_, nb_, nb_ * nb_, bb, w.nrhs, nb_, nb_ * w.nrhs, 1)
+        ok = ok and np.array_equal(gA[sa: sa + nb_ * nb_].view(np.uint8), a.view(np.uint8)) and \
+            np.array_equal(gB[sb: sb + nb_ * w.nrhs].view(np.uint8), bb.view(np.uint8))
+    parity = {"sampled_matrices": 3, "lu_and_x_bitwise_equal": bool(ok)}
+    for a_, b_ in sets:
+        a_.copy_(pA)
+        b_.copy_(pB)
+    ms = _timed(torch, step, reps, stream)
+    med, mean = float(np.median(ms)), float(np.mean(ms))
+    o = orders.astype(np.float64)
+    fl = float(np.sum(2.0 / 3.0 * o ** 3 + 2.0 * o ** 2 * w.nrhs))
+    tf = fl / (mean * 1e-3) / 1e12
+    out = {"n_min": int(orders.min()), "n_max": maxn, "n_mean": float(o.mean()), "nrhs": w.nrhs, "batch": w.batch,
+           "dtype": np.dtype(w.dtype).name, "op": "gesv_vbatched", "tier": "general", "input_sets": nsets,
+           "step_ms_median": med, "step_ms_mean": mean, "reps": reps,
+           "matrices_per_s": w.batch / (med * 1e-3), "gflops": fl / (med * 1e-3) / 1e9, "parity": parity,
+           "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tf / FP32_VALU_PEAK_TFLOPS, "traffic": None, "kernel_ms_mean": mean,
+                        "kernel_ms_median": med, "algorithmic_flops_per_launch": fl,
+                        "scope": "batchlu_gesv_vbatched (factor and solve launches)"}}
+    if with_cpu:
+        def run(mm, nt):
+            t0 = time.perf_counter()
+            for b in range(mm):
+                nb_, sa, sb = int(orders[b]), int(aoff[b]), int(boff[b])
+                a, bb = A[sa: sa + nb_ * nb_].copy(), B[sb: sb + nb_ * w.nrhs].copy()
+                oracle.gesv(a, nb_, nb_, nb_ * nb_, bb, w.nrhs, nb_, nb_ * w.nrhs, 1, nthreads=1)
+            return time.perf_counter() - t0, 1
+        cb = _bounded_oracle_rate(run, w.batch, cpu_s, "gesv, one matrix per call")
+        cb["value"], cb["cores"] = cb["single_core"]["value"], 1
+        cb["sample"] = cb["single_core"]["sample"] + " (one matrix per call, one host thread)"
+        out["cpu_baseline"] = cb
+    del sets, pA, pB
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -508,11 +675,16 @@ def main():
     results = {}
     for name in names:
         print(f"# {name}", file=sys.stderr, flush=True)
-        results[name] = measure(lib, torch, ALL_WORKLOADS[name], args.steps, args.warmup, args.cpu_run_s,
-                                not args.no_cpu_baseline)
+        wl = ALL_WORKLOADS[name]
+        fn = {"getrf_rect": measure_rect, "gesv_vbatched": measure_vbatch}.get(wl.op, measure)
+        results[name] = fn(lib, torch, wl, args.steps, args.warmup, args.cpu_run_s, not args.no_cpu_baseline)
     h = results[head]
     w = ALL_WORKLOADS[head]
-    ms_per_step = h["wall_ms_per_step"]
+    ms_per_step = h.get("wall_ms_per_step", h["step_ms_median"])
+    cfg = {"workload": head, "op": w.op}
+    for key in ("m", "n", "n_min", "n_max", "nrhs", "batch", "tier"):
+        if key in h:
+            cfg[key] = h[key]
     line = {
         "metric": METRIC,
         "value": w.batch / (ms_per_step * 1e-3),
@@ -526,8 +698,8 @@ def main():
         "vs_baseline": None,
         "dtype": {"float32": "f32", "float64": "f64", "complex64": "c64", "complex128": "c128"}[h["dtype"]],
         "data": "synthetic",
-        "config": {"workload": head, "op": w.op, "n": w.n, "nrhs": w.nrhs, "batch": w.batch, "tier": h["tier"]},
-        "gflops": algorithmic_flops(w) * w.batch / (ms_per_step * 1e-3) / 1e9,
+        "config": cfg,
+        "gflops": h["gflops"] * h["step_ms_median"] / ms_per_step,
         "roofline": h["roofline"],
         "parity": h["parity"],
     }

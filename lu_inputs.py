@@ -178,3 +178,51 @@ def chol_problem(w: Workload, batch: int | None = None):
     """(A, B) of a Cholesky workload, flat, ld = n (both triangles stored)."""
     b = w.batch if batch is None else min(batch, w.batch)
     return spd_problem(w.seed, w.dtype, w.n, w.nrhs, b)
+
+
+# LU shapes outside the square fixed-size batch: tall m x n panels, and a
+# batch whose square systems differ in order.
+RECT_WORKLOADS = {
+    "sgetrf_m512_n128_b2048": Workload("sgetrf_m512_n128_b2048", np.float32, 128, 0, 2048, "uniform",
+                                       "getrf_rect", 9),
+}
+RECT_ROWS = {"sgetrf_m512_n128_b2048": 512}
+
+
+@dataclass(frozen=True)
+class VWorkload:
+    """A batch of square systems of orders drawn uniformly from
+    [nmin, nmax] (the draw comes first from the seed), nrhs each."""
+    name: str
+    dtype: type
+    nmin: int
+    nmax: int
+    nrhs: int
+    batch: int
+    op: str
+    index: int
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.index
+
+
+VBATCH_WORKLOADS = {
+    "sgesv_vbatched_n16_256_r1_b4096": VWorkload("sgesv_vbatched_n16_256_r1_b4096", np.float32, 16, 256, 1, 4096,
+                                                 "gesv_vbatched", 10),
+}
+
+
+def vbatch_problem(w: VWorkload):
+    """(orders, A, B, a_offsets, b_offsets): matrix b is orders[b] square at
+    A[a_offsets[b]:] with lda = its order, its right-hand sides at
+    B[b_offsets[b]:] with ldb = its order; entries iid uniform[-1, 1]."""
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    orders = rng.integers(w.nmin, w.nmax + 1, w.batch).astype(np.int32)
+    na = orders.astype(np.int64) ** 2
+    nb = orders.astype(np.int64) * w.nrhs
+    a_off = np.concatenate([[0], np.cumsum(na)[:-1]])
+    b_off = np.concatenate([[0], np.cumsum(nb)[:-1]])
+    A = draw(rng, w.dtype, int(na.sum()))
+    B = draw(rng, w.dtype, int(nb.sum()))
+    return orders, A, B, a_off, b_off
