@@ -128,11 +128,11 @@ int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda,
  *  11 batch, 12 stream.
  * Rows n..ldc-1 of C are not written.  A matrix whose info was > 0 gets
  * inf/NaN entries (LAPACK returns info there and leaves the inverse
- * undefined).  Follows: BatchLAS "LU" page, getri paragraph (each row is
- * traced back through the interchange list in registers and the result is
- * written straight into C, so no permutation pass is needed): computed as
- * the NoTrans solve of A C = I, whose right-hand sides never exist in
- * memory.
+ * undefined).  Follows: BatchLAS "LU" page, getri row of the family table
+ * and the section on the shared interchange kernels (the pivoting is undone
+ * inside the solve, with no separate permutation pass): computed as the
+ * NoTrans solve of A C = I, whose right-hand sides are formed in registers
+ * and never stored.
  */
 int batchlu_getri(batchlu_dtype t, int n, const void* A, int lda,
                   long long strideA, const int* ipiv, long long strideP,

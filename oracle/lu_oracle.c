@@ -38,10 +38,10 @@
  *       then L^T z = w, then x = P^T z (transpositions in reverse order);
  *       A^H uses the conjugates of the factors.  Forward sums run in
  *       ascending k, backward sums in descending k, as in R5.
- *   R8  getri (inverse from the factors; the pages say only that each
- *       work-item traces its row back through the interchange list and
- *       writes straight into the output): C = A^{-1} as the solution of
- *       A C = I with the NoTrans solve of R5, out of place.
+ *   R8  getri (inverse from the factors; the LU page's getri row describes
+ *       only how the pivoting is undone without a separate pass, not the
+ *       arithmetic): C = A^{-1} as the solution of A C = I with the
+ *       NoTrans solve of R5, out of place.
  *
  * Arithmetic is in the working precision of the data type (the pivot choice
  * must be reproduced exactly); margins are reported in double.  Build with
