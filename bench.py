@@ -615,6 +615,90 @@ def measure_vbatch(lib, torch, w, steps, warmup, cpu_s, with_cpu):
     return out
 
 
+# ---------------------------------------------------------------------------
+# tier sweep: every tier that can run a shape, timed against the selector
+# ---------------------------------------------------------------------------
+
+SWEEP_NS = (8, 16, 32, 33, 48, 64, 96, 128, 256)
+SWEEP_BATCHES = (1, 16, 64, 256, 1024, 8192)
+SWEEP_NRHS = (1, 16)
+TIER_CODES = {"tiny": 1, "cta": 2, "blocked": 3, "cta_lds": 4}
+
+
+def _sweep_cells(only):
+    for dt in (0, 1, 2, 3):
+        for n in SWEEP_NS:
+            for batch in SWEEP_BATCHES:
+                if n * n * batch > 16 << 20:       # keep one input set at most 256 MiB
+                    continue
+                for nrhs in SWEEP_NRHS:
+                    for op in ("gesv", "posv"):
+                        if only and (dt, n, batch, nrhs, op) != only:
+                            continue
+                        yield dt, n, batch, nrhs, op
+
+
+def tier_sweep(lib, torch, only=None, reps=5):
+    """One JSON line per (dtype, n, batch, nrhs, op): the selector's tier and
+    the median event time of every tier that can run the shape (pinned with
+    batchlu_set_tier), on uniform[-1, 1] (gesv) or SPD (posv) inputs."""
+    st = torch.cuda.current_stream()
+    dts = {0: np.float32, 1: np.float64, 2: np.complex64, 3: np.complex128}
+    for dt, n, batch, nrhs, op in _sweep_cells(only):
+        if op == "gesv":
+            A, B = lu_inputs.random_problem(n * 131 + batch, dts[dt], n, nrhs, batch)
+        else:
+            A, B = lu_inputs.dominant_spd_problem(n * 131 + batch, dts[dt], n, nrhs, batch)
+        dA0, dB0 = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        ip = torch.empty(batch * n, dtype=torch.int32, device="cuda")
+        inf = torch.empty(batch, dtype=torch.int32, device="cuda")
+        code = 2 if op == "gesv" else 4
+        lib.batchlu_set_tier(0)
+        auto = lib.batchlu_select_tier(dt, code, n, nrhs, batch)
+        res = {"dtype": dt, "n": n, "batch": batch, "nrhs": nrhs, "op": op,
+               "auto": {v: k for k, v in TIER_CODES.items()}.get(auto, str(auto))}
+        for name, tc in TIER_CODES.items():
+            lib.batchlu_set_tier(tc)
+            if lib.batchlu_select_tier(dt, code, n, nrhs, batch) != tc:
+                continue
+            sets = [(dA0.clone(), dB0.clone()) for _ in range(reps + 1)]
+
+            def call(i):
+                a, b = sets[i]
+                if op == "gesv":
+                    lib.batchlu_gesv(dt, n, nrhs, a, n, n * n, ip, n, b, n, n * nrhs, inf, batch, stream=st)
+                else:
+                    lib.batchlu_posv(dt, "L", n, nrhs, a, n, n * n, b, n, n * nrhs, inf, batch, stream=st)
+            call(reps)                           # warm-up on the spare set
+            res[name + "_ms"] = float(np.median(_timed(torch, call, reps, st)))
+            del sets
+        lib.batchlu_set_tier(0)
+        print(json.dumps(res), flush=True)
+
+
+def sweep_summary(path):
+    """Markdown table of a tier sweep: the fastest tier per cell, the
+    selector's choice and its time over the fastest."""
+    rows = [json.loads(line) for line in open(path) if line.startswith("{")]
+    tn = {0: "f32", 1: "f64", 2: "c64", 3: "c128"}
+    worst = []
+    print("| op | type | n | batch | nrhs | selector | fastest | times (ms) | selector / fastest |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        t = {k[:-3]: v for k, v in r.items() if k.endswith("_ms")}
+        if not t:
+            continue
+        best = min(t, key=t.get)
+        ratio = t.get(r["auto"], float("nan")) / t[best]
+        worst.append(ratio)
+        print(f"| {r['op']} | {tn[r['dtype']]} | {r['n']} | {r['batch']} | {r['nrhs']} | {r['auto']} | {best} | "
+              + ", ".join(f"{k} {v:.4f}" for k, v in sorted(t.items())) + f" | {ratio:.2f} |")
+    w = np.array(worst)
+    print(f"\n{len(w)} cells; selector within 5 % of the fastest tier in {int(np.sum(w <= 1.05))}, "
+          f"within 10 % in {int(np.sum(w <= 1.10))}; worst {np.nanmax(w):.2f}, geometric mean "
+          f"{float(np.exp(np.nanmean(np.log(w)))):.3f}.")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -630,9 +714,17 @@ def main():
                          "(FETCH_SIZE, WRITE_SIZE) taken with --copy-probe-mb; no GPU needed")
     ap.add_argument("--kernel-counters", nargs="+", metavar="DB",
                     help="print per-kernel means of the counters in rocprofv3 --pmc databases; no GPU needed")
+    ap.add_argument("--tier-sweep", action="store_true",
+                    help="time every tier that can run each shape of a grid against the selector (JSON lines)")
+    ap.add_argument("--sweep-cell", nargs=5, metavar=("DTYPE", "N", "BATCH", "NRHS", "OP"),
+                    help="restrict --tier-sweep to one cell (dtype code 0..3, op gesv or posv)")
+    ap.add_argument("--sweep-summary", metavar="JSONL", help="render a tier sweep as a table; no GPU needed")
     ap.add_argument("--trace-summary", metavar="DB",
                     help="print per-kernel times of a rocprofv3 --kernel-trace database; no GPU needed")
     args = ap.parse_args()
+    if args.sweep_summary:
+        sweep_summary(args.sweep_summary)
+        return
     if args.trace_summary:
         kernel_trace_table(args.trace_summary)
         return
@@ -669,6 +761,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.tier_sweep:
+        only = None
+        if args.sweep_cell:
+            d, nn, bb, rr, oo = args.sweep_cell
+            only = (int(d), int(nn), int(bb), int(rr), oo)
+        tier_sweep(lib, torch, only)
+        return
 
     names = ORDER if args.workload == "all" else [args.workload]
     head = HEADLINE if args.workload == "all" else args.workload

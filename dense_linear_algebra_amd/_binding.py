@@ -16,8 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbatchlu.so")
 
 R32, R64, C64, C128 = 0, 1, 2, 3
-TIER_AUTO, TIER_TINY, TIER_CTA, TIER_BLOCKED = 0, 1, 2, 3
-TIER_NAMES = {TIER_TINY: "tiny", TIER_CTA: "cta", TIER_BLOCKED: "blocked"}
+TIER_AUTO, TIER_TINY, TIER_CTA, TIER_BLOCKED, TIER_CTA_LDS = 0, 1, 2, 3, 4
+TIER_NAMES = {TIER_TINY: "tiny", TIER_CTA: "cta", TIER_BLOCKED: "blocked", TIER_CTA_LDS: "cta_lds"}
 OK, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_LAUNCH = 0, -100, -101, -102
 
 _lib = None

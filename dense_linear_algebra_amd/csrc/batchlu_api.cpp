@@ -55,6 +55,11 @@ bool tier_can_run(int tier, int t, int op, int n, int nrhs) {
     case BATCHLU_TIER_BLOCKED:
         if (op == OP_GETRS) return blocked_supported(t, n) || getrs_rows_supported(t, n);
         return blocked_supported(t, n);
+    case BATCHLU_TIER_CTA_LDS:
+        if (op == OP_GETRS) return getrs_rows_supported(t, n) && cta_lds_supported(t, n, 0, MODE_GETRF);
+        if (op == OP_GESV) return cta_lds_supported(t, n, nrhs, MODE_GESV) ||
+                                  (cta_lds_supported(t, n, 0, MODE_GETRF) && getrs_rows_supported(t, n));
+        return cta_lds_supported(t, n, 0, MODE_GETRF);
     default:
         return false;
     }
@@ -80,6 +85,7 @@ int run_getrf(int tier, int t, const Problem& p, hipStream_t s) {
     case BATCHLU_TIER_TINY: return status_of(register_launch(t, p, MODE_GETRF, false, s));
     case BATCHLU_TIER_CTA: return status_of(register_launch(t, p, MODE_GETRF, true, s));
     case BATCHLU_TIER_BLOCKED: return status_of(blocked_getrf(t, p, s));
+    case BATCHLU_TIER_CTA_LDS: return status_of(cta_lds_launch(t, p, MODE_GETRF, s));
     default: return BATCHLU_ERR_CAPACITY;
     }
 }
@@ -197,7 +203,9 @@ int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda, long long s
     Problem p;
     p.n = n; p.nrhs = nrhs; p.batch = batch; p.A = A; p.lda = lda; p.sA = strideA;
     p.ipiv = ipiv; p.sP = strideP; p.info = info; p.B = B; p.ldb = ldb; p.sB = strideB;
-    if (tier != BATCHLU_TIER_BLOCKED && nrhs > 0 &&
+    if (tier == BATCHLU_TIER_CTA_LDS && nrhs > 0 && cta_lds_supported(t, n, nrhs, MODE_GESV))
+        return status_of(cta_lds_launch(t, p, MODE_GESV, stream));
+    if ((tier == BATCHLU_TIER_TINY || tier == BATCHLU_TIER_CTA) && nrhs > 0 &&
         register_supported(t, n, nrhs, MODE_GESV, tier == BATCHLU_TIER_CTA))
         return status_of(register_launch(t, p, MODE_GESV, tier == BATCHLU_TIER_CTA, stream));
     int st = run_getrf(tier, t, p, stream);
@@ -395,7 +403,7 @@ int batchlu_select_tier(batchlu_dtype t, int op, int n, int nrhs, int batch) {
 
 int batchlu_set_tier(int tier) {
     const int prev = tier_pin();
-    if (tier < BATCHLU_TIER_AUTO || tier > BATCHLU_TIER_BLOCKED) return -1;
+    if (tier < BATCHLU_TIER_AUTO || tier > BATCHLU_TIER_CTA_LDS) return -1;
     g_tier_pin.store(tier);
     return prev;
 }

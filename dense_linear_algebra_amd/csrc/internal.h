@@ -36,6 +36,11 @@ hipError_t register_launch(int dtype, const Problem& p, int mode, bool one_wave_
 bool getrs_rows_supported(int dtype, int n);
 hipError_t getrs_rows_launch(int dtype, const Problem& p, hipStream_t s);
 
+// LDS-staged work-group tier: one work-group per matrix, [A | B] in LDS
+// (n <= 128, complex double 64; gesv fused for nrhs <= 16).
+bool cta_lds_supported(int dtype, int n, int nrhs, int mode);
+hipError_t cta_lds_launch(int dtype, const Problem& p, int mode, hipStream_t s);
+
 // Blocked tier in one work-group per matrix (real types, n <= 256).
 bool blocked_fused_supported(int dtype, int n, int lda);
 hipError_t blocked_fused_getrf(int dtype, const Problem& p, hipStream_t s);

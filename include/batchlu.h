@@ -59,6 +59,7 @@ typedef enum {
 #define BATCHLU_TIER_TINY 1    /* several matrices per wavefront, rows in VGPRs */
 #define BATCHLU_TIER_CTA 2     /* one work-group per matrix, rows in VGPRs       */
 #define BATCHLU_TIER_BLOCKED 3 /* nb = 32 right-looking: panel, laswp, trsm, gemm */
+#define BATCHLU_TIER_CTA_LDS 4 /* one work-group per matrix, [A | B] staged in LDS */
 
 /*
  * batchlu_getrf -- LU with partial pivoting of `batch` n x n matrices, in place.

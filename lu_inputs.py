@@ -226,3 +226,21 @@ def vbatch_problem(w: VWorkload):
     A = draw(rng, w.dtype, int(na.sum()))
     B = draw(rng, w.dtype, int(nb.sum()))
     return orders, A, B, a_off, b_off
+
+
+def dominant_spd_problem(seed: int, dtype, n: int, nrhs: int, batch: int):
+    """Cheap Hermitian positive definite matrices for timing sweeps:
+    (M + M^H)/2 + n I with M iid uniform[-1, 1] (complex: both parts), made
+    exactly Hermitian in double and rounded; every off-diagonal row sum is
+    below n, so the matrix is positive definite (Gershgorin).  B iid
+    uniform[-1, 1]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt = np.dtype(dtype)
+    wide = np.complex128 if dt.kind == "c" else np.float64
+    M = draw(rng, wide, batch * n * n).reshape(batch, n, n)
+    M = (M + np.conj(np.swapaxes(M, 1, 2))) / 2
+    idx = np.arange(n)
+    M[:, idx, idx] = M[:, idx, idx].real + n
+    A = np.ascontiguousarray(np.swapaxes(M, 1, 2)).reshape(-1).astype(dt)
+    B = draw(rng, dt, batch * n * nrhs)
+    return A, B
