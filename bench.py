@@ -676,14 +676,16 @@ def tier_sweep(lib, torch, only=None, reps=5):
         print(json.dumps(res), flush=True)
 
 
-def sweep_summary(path):
-    """Markdown table of a tier sweep: the fastest tier per cell, the
-    selector's choice and its time over the fastest."""
+def sweep_summary(path, full=False):
+    """A tier sweep rendered as markdown: per operation and type, a grid over
+    n (rows) and batch (columns) of the selector's tier for nrhs 1 / 16, with
+    its time over the fastest tier's where that is above 1.02; then the
+    cells where another tier was faster, and the totals.  full=True prints
+    every cell's times instead of the grids."""
     rows = [json.loads(line) for line in open(path) if line.startswith("{")]
     tn = {0: "f32", 1: "f64", 2: "c64", 3: "c128"}
-    worst = []
-    print("| op | type | n | batch | nrhs | selector | fastest | times (ms) | selector / fastest |")
-    print("|---|---|---|---|---|---|---|---|---|")
+    letter = {"tiny": "t", "cta": "c", "cta_lds": "l", "blocked": "b"}
+    cells, worst = [], []
     for r in rows:
         t = {k[:-3]: v for k, v in r.items() if k.endswith("_ms")}
         if not t:
@@ -691,8 +693,41 @@ def sweep_summary(path):
         best = min(t, key=t.get)
         ratio = t.get(r["auto"], float("nan")) / t[best]
         worst.append(ratio)
-        print(f"| {r['op']} | {tn[r['dtype']]} | {r['n']} | {r['batch']} | {r['nrhs']} | {r['auto']} | {best} | "
-              + ", ".join(f"{k} {v:.4f}" for k, v in sorted(t.items())) + f" | {ratio:.2f} |")
+        cells.append((r, t, best, ratio))
+    if full:
+        print("| op | type | n | batch | nrhs | selector | fastest | times (ms) | selector / fastest |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for r, t, best, ratio in cells:
+            print(f"| {r['op']} | {tn[r['dtype']]} | {r['n']} | {r['batch']} | {r['nrhs']} | {r['auto']} | {best} | "
+                  + ", ".join(f"{k} {v:.4f}" for k, v in sorted(t.items())) + f" | {ratio:.2f} |")
+    else:
+        print("Tiers: t = tiny (register), c = cta (register), l = cta_lds (LDS-staged), b = blocked. "
+              "Each entry is the selector's tier for nrhs 1 / nrhs 16, with (its time / the fastest "
+              "tier's time) where above 1.02.\n")
+        grid = {}
+        for r, t, best, ratio in cells:
+            mark = letter.get(r["auto"], r["auto"]) + (f" ({ratio:.2f})" if ratio > 1.02 else "")
+            grid.setdefault((r["op"], r["dtype"]), {}).setdefault((r["n"], r["batch"]), {})[r["nrhs"]] = mark
+        for (op, dt), g in grid.items():
+            ns = sorted({k[0] for k in g})
+            bs = sorted({k[1] for k in g})
+            print(f"**{op} {tn[dt]}**\n")
+            print("| n \\ batch | " + " | ".join(str(b) for b in bs) + " |")
+            print("|---" * (len(bs) + 1) + "|")
+            for n in ns:
+                ent = []
+                for b in bs:
+                    c = g.get((n, b), {})
+                    ent.append(" / ".join(c[k] for k in sorted(c)) if c else "")
+                print(f"| {n} | " + " | ".join(ent) + " |")
+            print()
+        print("Cells where another tier was more than 2 % faster:\n")
+        print("| op | type | n | batch | nrhs | selector | fastest | times (ms) | ratio |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for r, t, best, ratio in cells:
+            if ratio > 1.02:
+                print(f"| {r['op']} | {tn[r['dtype']]} | {r['n']} | {r['batch']} | {r['nrhs']} | {r['auto']} | "
+                      f"{best} | " + ", ".join(f"{k} {v:.4f}" for k, v in sorted(t.items())) + f" | {ratio:.2f} |")
     w = np.array(worst)
     print(f"\n{len(w)} cells; selector within 5 % of the fastest tier in {int(np.sum(w <= 1.05))}, "
           f"within 10 % in {int(np.sum(w <= 1.10))}; worst {np.nanmax(w):.2f}, geometric mean "
@@ -718,12 +753,13 @@ def main():
                     help="time every tier that can run each shape of a grid against the selector (JSON lines)")
     ap.add_argument("--sweep-cell", nargs=5, metavar=("DTYPE", "N", "BATCH", "NRHS", "OP"),
                     help="restrict --tier-sweep to one cell (dtype code 0..3, op gesv or posv)")
-    ap.add_argument("--sweep-summary", metavar="JSONL", help="render a tier sweep as a table; no GPU needed")
+    ap.add_argument("--sweep-summary", metavar="JSONL", help="render a tier sweep as tables; no GPU needed")
+    ap.add_argument("--sweep-full", action="store_true", help="with --sweep-summary: every cell's times")
     ap.add_argument("--trace-summary", metavar="DB",
                     help="print per-kernel times of a rocprofv3 --kernel-trace database; no GPU needed")
     args = ap.parse_args()
     if args.sweep_summary:
-        sweep_summary(args.sweep_summary)
+        sweep_summary(args.sweep_summary, args.sweep_full)
         return
     if args.trace_summary:
         kernel_trace_table(args.trace_summary)

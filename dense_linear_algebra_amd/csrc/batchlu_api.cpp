@@ -2,13 +2,17 @@
 //
 // Tier selection (BatchLAS "LU" page, family table and routing tables): the
 // pages rank register-resident kernels first for small n, a one-work-group
-// kernel for mid n and the blocked right-looking driver above.  On gfx950
-// the register tiers hold a matrix in VGPRs:
+// kernel for mid n and the blocked right-looking driver above, keyed on the
+// shape and the batch.  On gfx950 the register tiers hold a matrix in VGPRs:
 //   tiny    n <= 32: several matrices per wavefront;
 //   cta     32 < n <= 64 (complex double: none): one wavefront per matrix;
-//   blocked larger n, nb = 32.
+//   blocked larger n, nb = 32;
+//   cta_lds one work-group per matrix with the matrix in LDS (n <= 128):
+//           the fastest gesv for small batches in the cells listed below,
+//           slower than the others at batch >= 1024 and at n >= 96.
 // gesv runs fused (factor + forward + back in one kernel) in the register
-// tiers while nrhs <= 16; otherwise it is getrf followed by getrs.
+// tiers while nrhs <= 16, except where the measured crossovers below pick
+// the composed factor-then-solve; otherwise it is getrf followed by getrs.
 #include <atomic>
 #include <climits>
 #include <cstdlib>
@@ -65,17 +69,60 @@ bool tier_can_run(int tier, int t, int op, int n, int nrhs) {
     }
 }
 
-int auto_tier(int t, int op, int n, int nrhs) {
+// Measured crossovers (MI355X, every tier timed on a grid of type x n in
+// {8..256} x batch in {1..8192} x nrhs in {1, 16}; `bench.py --tier-sweep`,
+// summary in profiles/selector_sweep.md).  The register tiers win getrf
+// everywhere they run, and gesv everywhere at batch >= 1024; at batch <= 256
+// with more than 8 right-hand sides the fused kernel's one wavefront per
+// matrix carries the whole solve serially, and factoring in the register or
+// blocked tier then solving with one work-group per (matrix, RHS tile) is
+// faster for these orders (ratios 0.6 - 0.95 of the fused time).
+constexpr int kSmallBatch = 256;
+
+bool lu_composed_wins(int t, int n) {
+    switch (t) {
+    case BATCHLU_R32: return n <= 8;
+    case BATCHLU_R64: return n >= 16;
+    case BATCHLU_C64: return n >= 16 && n <= 32;
+    default: return n >= 16;
+    }
+}
+
+// gesv at batch <= 256 (same sweep): the LDS-staged work-group tier is the
+// fastest for complex double at 33 <= n <= 64 (no register tier there;
+// 0.54 - 0.94 of the blocked time) and, with more than 8 right-hand sides,
+// for these small orders (0.6 - 0.9 of the next best).
+bool lds_wins(int t, int n, int nrhs) {
+    switch (t) {
+    case BATCHLU_R32: return nrhs > 8 && n <= 8;
+    case BATCHLU_R64: return nrhs > 8 && (n <= 16 || (n >= 33 && n <= 40));
+    case BATCHLU_C64: return nrhs > 8 && (n <= 16 || (n >= 33 && n <= 48));
+    default: return (n >= 33 && n <= 64) || (nrhs > 8 && n <= 16);
+    }
+}
+
+int auto_tier(int t, int op, int n, int nrhs, int batch) {
+    // float n <= 8 with many right-hand sides: the LDS tier still wins at
+    // batch 1024 (0.67 of the next best), not at 8192
+    if (op == OP_GESV && t == BATCHLU_R32 && n <= 8 && nrhs > 8 && batch <= 4 * kSmallBatch &&
+        tier_can_run(BATCHLU_TIER_CTA_LDS, t, op, n, nrhs))
+        return BATCHLU_TIER_CTA_LDS;
+    if (op == OP_GESV && batch <= kSmallBatch && nrhs > 0) {
+        if (lds_wins(t, n, nrhs) && tier_can_run(BATCHLU_TIER_CTA_LDS, t, op, n, nrhs))
+            return BATCHLU_TIER_CTA_LDS;
+        if (nrhs > 8 && lu_composed_wins(t, n) && tier_can_run(BATCHLU_TIER_BLOCKED, t, op, n, nrhs))
+            return BATCHLU_TIER_BLOCKED;
+    }
     const int order[3] = {BATCHLU_TIER_TINY, BATCHLU_TIER_CTA, BATCHLU_TIER_BLOCKED};
     for (int tier : order)
         if (tier_can_run(tier, t, op, n, nrhs)) return tier;
     return BATCHLU_ERR_CAPACITY;
 }
 
-int choose(int t, int op, int n, int nrhs) {
+int choose(int t, int op, int n, int nrhs, int batch) {
     const int pin = tier_pin();
     if (pin != BATCHLU_TIER_AUTO) return tier_can_run(pin, t, op, n, nrhs) ? pin : BATCHLU_ERR_CAPACITY;
-    return auto_tier(t, op, n, nrhs);
+    return auto_tier(t, op, n, nrhs, batch);
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? BATCHLU_OK : BATCHLU_ERR_LAUNCH; }
@@ -114,7 +161,7 @@ int batchlu_getrf(batchlu_dtype t, int n, void* A, int lda, long long strideA, i
     if (!A) return -3;
     if (!ipiv) return -6;
     if (!info) return -8;
-    const int tier = choose(t, OP_GETRF, n, 0);
+    const int tier = choose(t, OP_GETRF, n, 0, batch);
     if (tier < 0) return tier;
     Problem p;
     p.n = n; p.batch = batch; p.A = A; p.lda = lda; p.sA = strideA;
@@ -142,7 +189,7 @@ int batchlu_getrs(batchlu_dtype t, char trans, int n, int nrhs, const void* A, i
     if (!ipiv) return -8;
     if (!B) return -10;
     if (op != 0 && !getrs_rows_supported(t, n)) return BATCHLU_ERR_UNSUPPORTED;   // n > 1024
-    const int tier = choose(t, OP_GETRS, n, nrhs);
+    const int tier = choose(t, OP_GETRS, n, nrhs, batch);
     if (tier < 0) return tier;
     Problem p;
     p.n = n; p.nrhs = nrhs; p.batch = batch; p.A = const_cast<void*>(A); p.lda = lda; p.sA = strideA;
@@ -198,7 +245,7 @@ int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda, long long s
     if (!ipiv) return -7;
     if (nrhs > 0 && !B) return -9;
     if (!info) return -12;
-    const int tier = choose(t, OP_GESV, n, nrhs);
+    const int tier = choose(t, OP_GESV, n, nrhs, batch);
     if (tier < 0) return tier;
     Problem p;
     p.n = n; p.nrhs = nrhs; p.batch = batch; p.A = A; p.lda = lda; p.sA = strideA;
@@ -228,11 +275,28 @@ namespace {
 bool valid_uplo(char u) { return u == 'L' || u == 'l' || u == 'U' || u == 'u'; }
 bool is_upper(char u) { return u == 'U' || u == 'u'; }
 
-int chol_tier(int t, int n) {
+// posv at batch <= 256 (same sweep): the blocked potrf plus the one-launch
+// solve beats the fused register kernel for these orders with more than 8
+// right-hand sides, and for double at n >= 64 with any number.
+bool chol_composed_wins(int t, int n, int nrhs) {
+    if (t == BATCHLU_R64 && n >= 64) return true;
+    if (nrhs <= 8) return false;
+    switch (t) {
+    case BATCHLU_R32: return n >= 48;
+    case BATCHLU_R64: return n >= 32;
+    case BATCHLU_C64: return n >= 32;
+    default: return n >= 16;
+    }
+}
+
+int chol_tier(int t, int op, int n, int nrhs, int batch) {
     const int pin = tier_pin();
     const bool reg = chol_register_supported(t, n), blk = chol_blocked_supported(t, n);
     if (pin == BATCHLU_TIER_TINY || pin == BATCHLU_TIER_CTA) return reg ? pin : BATCHLU_ERR_CAPACITY;
     if (pin == BATCHLU_TIER_BLOCKED) return blk ? pin : BATCHLU_ERR_CAPACITY;
+    if (pin == BATCHLU_TIER_CTA_LDS) return BATCHLU_ERR_CAPACITY;   // no LDS-staged Cholesky
+    if (reg && blk && op == 4 && batch <= kSmallBatch && nrhs > 0 && chol_composed_wins(t, n, nrhs))
+        return BATCHLU_TIER_BLOCKED;
     return reg ? BATCHLU_TIER_CTA : blk ? BATCHLU_TIER_BLOCKED : BATCHLU_ERR_CAPACITY;
 }
 
@@ -256,7 +320,7 @@ int batchlu_potrf(batchlu_dtype t, char uplo, int n, void* A, int lda, long long
     if (n == 0 || batch == 0) return BATCHLU_OK;
     if (!A) return -4;
     if (!info) return -7;
-    const int tier = chol_tier(t, n);
+    const int tier = chol_tier(t, 3, n, 0, batch);
     if (tier < 0) return tier;
     Problem p;
     p.n = n; p.batch = batch; p.A = A; p.lda = lda; p.sA = strideA; p.info = info; p.upper = is_upper(uplo);
@@ -299,7 +363,7 @@ int batchlu_posv(batchlu_dtype t, char uplo, int n, int nrhs, void* A, int lda, 
     if (!A) return -5;
     if (nrhs > 0 && !B) return -8;
     if (!info) return -11;
-    const int tier = chol_tier(t, n);
+    const int tier = chol_tier(t, 4, n, nrhs, batch);
     if (tier < 0) return tier;
     if (nrhs > 0 && !chol_solve_supported(t, n)) return BATCHLU_ERR_CAPACITY;
     Problem p;
@@ -397,8 +461,8 @@ int batchlu_select_tier(batchlu_dtype t, int op, int n, int nrhs, int batch) {
     if (n < 0) return -3;
     if (nrhs < 0) return -4;
     if (batch < 0) return -5;
-    if (op >= 3) return chol_tier(t, n);   // 3 potrf, 4 posv
-    return choose(t, op, n, nrhs);
+    if (op >= 3) return chol_tier(t, op, n, nrhs, batch);   // 3 potrf, 4 posv
+    return choose(t, op, n, nrhs, batch);
 }
 
 int batchlu_set_tier(int tier) {

@@ -120,3 +120,29 @@ def test_tier_pin_refuses_instead_of_truncating():
                                  raise_on_error=False) == -101
     finally:
         lib.batchlu_set_tier(prev)
+
+
+@pytest.mark.parametrize("t,op,n,nrhs,batch,tier", [
+    # gesv, 16 right-hand sides, small batch: factor then solve (blocked)
+    (lib.R64, 2, 64, 16, 64, lib.TIER_BLOCKED),
+    (lib.R64, 2, 64, 16, 8192, lib.TIER_CTA),
+    # complex double 33..64: the LDS-staged work-group tier at small batch
+    (lib.C128, 2, 48, 1, 64, lib.TIER_CTA_LDS),
+    (lib.C128, 2, 48, 1, 8192, lib.TIER_BLOCKED),
+    # float n <= 8 with many right-hand sides: LDS tier up to batch 1024
+    (lib.R32, 2, 8, 16, 1024, lib.TIER_CTA_LDS),
+    (lib.R32, 2, 8, 16, 8192, lib.TIER_TINY),
+    # getrf keeps the register tiers at every batch
+    (lib.R64, 0, 64, 0, 1, lib.TIER_CTA),
+    (lib.C64, 0, 16, 0, 16, lib.TIER_TINY),
+    # posv (op 4): double n >= 64 at small batch goes to the blocked driver
+    (lib.R64, 4, 64, 1, 64, lib.TIER_BLOCKED),
+    (lib.R64, 4, 64, 1, 4096, lib.TIER_CTA),
+    (lib.C128, 4, 16, 16, 16, lib.TIER_BLOCKED),
+    (lib.C128, 3, 16, 0, 16, lib.TIER_CTA),
+])
+def test_selector_uses_the_measured_crossovers(t, op, n, nrhs, batch, tier):
+    """The selector keys on the batch and the number of right-hand sides as
+    well as the type and order (crossovers measured by bench.py
+    --tier-sweep)."""
+    assert lib.batchlu_select_tier(t, op, n, nrhs, batch) == tier
