@@ -57,7 +57,7 @@ bool tier_can_run(int tier, int t, int op, int n, int nrhs) {
         return register_supported(t, n, 0, MODE_GETRF, one_wave);
     }
     case BATCHLU_TIER_BLOCKED:
-        if (op == OP_GETRS) return blocked_supported(t, n) || getrs_rows_supported(t, n);
+        if (op == OP_GETRS) return blocked_getrs_supported(t, n) || getrs_rows_supported(t, n);
         return blocked_supported(t, n);
     case BATCHLU_TIER_CTA_LDS:
         if (op == OP_GETRS) return getrs_rows_supported(t, n) && cta_lds_supported(t, n, 0, MODE_GETRF);
@@ -188,7 +188,7 @@ int batchlu_getrs(batchlu_dtype t, char trans, int n, int nrhs, const void* A, i
     if (!A) return -5;
     if (!ipiv) return -8;
     if (!B) return -10;
-    if (op != 0 && !getrs_rows_supported(t, n)) return BATCHLU_ERR_UNSUPPORTED;   // n > 1024
+    if (!getrs_rows_supported(t, n) && !blocked_getrs_supported(t, n)) return BATCHLU_ERR_UNSUPPORTED;
     const int tier = choose(t, OP_GETRS, n, nrhs, batch);
     if (tier < 0) return tier;
     Problem p;
@@ -220,12 +220,13 @@ int batchlu_getri(batchlu_dtype t, int n, const void* A, int lda, long long stri
         const char* c0 = (const char*)C;
         if (c0 < a0 + ea && a0 < c0 + ec) return -8;
     }
-    if (!getrs_rows_supported(t, n)) return BATCHLU_ERR_UNSUPPORTED;   // n > 1024
+    if (!getrs_rows_supported(t, n) && !blocked_getrs_supported(t, n)) return BATCHLU_ERR_UNSUPPORTED;
     Problem p;
     p.n = n; p.nrhs = n; p.batch = batch; p.A = const_cast<void*>(A); p.lda = lda; p.sA = strideA;
     p.ipiv = const_cast<int*>(ipiv); p.sP = strideP; p.B = C; p.ldb = ldc; p.sB = strideC;
     p.inverse = true;
-    return status_of(getrs_rows_launch(t, p, stream));
+    if (getrs_rows_supported(t, n)) return status_of(getrs_rows_launch(t, p, stream));
+    return status_of(blocked_getrs(t, p, stream));
 }
 
 int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda, long long strideA, int* ipiv,

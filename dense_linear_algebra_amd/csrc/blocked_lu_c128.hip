@@ -6,5 +6,6 @@ namespace batchlu {
 
 hipError_t blocked_getrf_c128(const Problem& p, hipStream_t s) { return getrf_t<cplx<double>>(p, s); }
 hipError_t blocked_getrs_c128(const Problem& p, hipStream_t s) { return getrs_t<cplx<double>>(p, s); }
+hipError_t blocked_getri_c128(const Problem& p, hipStream_t s) { return getri_t<cplx<double>>(p, s); }
 
 }  // namespace batchlu

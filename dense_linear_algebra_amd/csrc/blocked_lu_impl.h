@@ -338,17 +338,20 @@ __device__ inline int trace_back(const int* sp, int w, int x) {
     return x;
 }
 
-// Solve with the 32 x 32 diagonal block of T for columns [c0, c0 + 64) of X.
-//   lower unit (UPPER = false): x_f -= l_fm x_m, m ascending;
-//   upper (UPPER = true): x_m /= u_mm then x_f -= u_fm x_m, m descending.
+// Solve with the 32 x 32 diagonal block of op(T) for columns [c0, c0 + 64)
+// of X, where op(T) is T (aop 0), T^T (aop 1) or T^H (aop 2):
+//   lower, unit diagonal: x_f -= t_fm x_m, m ascending;
+//   lower: x_m /= t_mm then x_f -= t_fm x_m, m ascending;
+//   upper: x_m /= t_mm then x_f -= t_fm x_m, m descending;
+//   upper, unit diagonal: x_f -= t_fm x_m, m descending.
 // With `swap` the rows of X are first permuted by the w transpositions in
 // ipiv[j0 .. j0 + w) (getrf right-hand interchange): rows j0.. j0+w-1 get the
 // solved values, displaced rows below are copied to their new places.
-template <typename T, bool UPPER>
+template <typename T, bool UPPER, bool UNIT>
 __global__ void __launch_bounds__(64) trsm_block_kernel(const void* Tmat, int ldt, long long sT, void* Xmat,
                                                         int ldx, long long sX, int r0, int w, int ncols,
                                                         int ctiles, const int* ipiv, long long sP, bool swap,
-                                                        const int* info)
+                                                        const int* info, int aop)
 {
     using O = ops<T>;
     __shared__ T tri[NBP][NBP + 1];
@@ -373,7 +376,16 @@ __global__ void __launch_bounds__(64) trsm_block_kernel(const void* Tmat, int ld
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int e = e0 + u * 64;
-            if (e < w * w) tri[e % w][e / w] = v[u];
+            if (e >= w * w) continue;
+            if (aop == 0) {
+                tri[e % w][e / w] = v[u];
+            } else {
+                T x = v[u];
+                if constexpr (O::is_complex) {
+                    if (aop == 2) x.im = -x.im;
+                }
+                tri[e / w][e % w] = x;
+            }
         }
     }
     if (swap) {
@@ -412,6 +424,7 @@ __global__ void __launch_bounds__(64) trsm_block_kernel(const void* Tmat, int ld
         for (int mm = 0; mm < NBP; ++mm) {
             if (mm >= w) continue;
             if (swap && O::metric(tri[mm][mm]) == typename O::R(0)) continue;
+            if (!UNIT) x[mm] = O::div(x[mm], tri[mm][mm]);
 #pragma unroll
             for (int f = 0; f < NBP; ++f)
                 if (f > mm && f < w) O::fms(x[f], tri[f][mm], x[mm]);
@@ -420,7 +433,7 @@ __global__ void __launch_bounds__(64) trsm_block_kernel(const void* Tmat, int ld
 #pragma unroll
         for (int mm = NBP - 1; mm >= 0; --mm) {
             if (mm >= w) continue;
-            x[mm] = O::div(x[mm], tri[mm][mm]);
+            if (!UNIT) x[mm] = O::div(x[mm], tri[mm][mm]);
 #pragma unroll
             for (int f = 0; f < NBP; ++f)
                 if (f < mm) O::fms(x[f], tri[f][mm], x[mm]);
@@ -448,18 +461,26 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ inline void tile_load(T (*As)[TT], T (*Bs)[TT], const T* Ap, int lda_, const T* Bp, int ldb_,
-                                 int M, int N, int K, int tid, int nthr, bool negate)
+                                 int M, int N, int K, int tid, int nthr, bool negate, int aop = 0)
 {
     using O = ops<T>;
-    // loads issued in batches of eight per thread before their LDS stores
+    // op(A) element (i, k) is Ap[i + k lda] (aop 0), or Ap[k + i lda] (aop 1),
+    // conjugated for aop 2; the transposed read walks k fastest so that it
+    // stays coalesced.  Loads issued in batches of eight per thread before
+    // their LDS stores.
     for (int e0 = tid; e0 < TT * K; e0 += nthr * 8) {
         T va[8], vb[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int e = e0 + u * nthr;
             if (e < TT * K) {
-                const int i = e % TT, k = e / TT;
-                va[u] = i < M ? Ap[i + (long long)k * lda_] : O::zero();
+                if (aop == 0) {
+                    const int i = e % TT, k = e / TT;
+                    va[u] = i < M ? Ap[i + (long long)k * lda_] : O::zero();
+                } else {
+                    const int k = e % K, i = e / K;
+                    va[u] = i < M ? Ap[k + (long long)i * lda_] : O::zero();
+                }
                 const int k2 = e % K, j = e / K;
                 vb[u] = j < N ? Bp[k2 + (long long)j * ldb_] : O::zero();
             }
@@ -469,11 +490,15 @@ __device__ inline void tile_load(T (*As)[TT], T (*Bs)[TT], const T* Ap, int lda_
             const int e = e0 + u * nthr;
             if (e < TT * K) {
                 T v = va[u];
+                if constexpr (O::is_complex) {
+                    if (aop == 2) v.im = -v.im;
+                }
                 if (negate) {
                     if constexpr (O::is_complex) { v.re = -v.re; v.im = -v.im; }
                     else v = -v;
                 }
-                As[e / TT][e % TT] = v;
+                if (aop == 0) As[e / TT][e % TT] = v;
+                else As[e % K][e / K] = v;
                 Bs[e % K][e / K] = vb[u];
             }
         }
@@ -632,7 +657,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) gemm_mfma_kernel(const void* Am, int lda_, long long sA, const void* Bm,
                                                         int ldb_, long long sB, void* Cm, int ldc, long long sC,
                                                         int M, int N, int K, int mtiles, int ntiles, int kdir,
-                                                        const int* info)
+                                                        const int* info, int aop)
 {
     __shared__ T As[NBP][TT];
     __shared__ T Bs[NBP][TT];
@@ -641,11 +666,11 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const void* Am, int lda_
     const int t = (int)(blockIdx.x % tiles);
     const int i0 = (t % mtiles) * TT, jt0 = (t / mtiles) * TT;
     if (info && info[mat] != 0) return;
-    const T* Ap = (const T*)Am + mat * sA + i0;
+    const T* Ap = (const T*)Am + mat * sA + (aop ? (long long)i0 * lda_ : (long long)i0);
     const T* Bp = (const T*)Bm + mat * sB + (long long)jt0 * ldb_;
     T* Cp = (T*)Cm + mat * sC + i0 + (long long)jt0 * ldc;
     const int Mt = min(TT, M - i0), Nt = min(TT, N - jt0);
-    tile_load<T>(As, Bs, Ap, lda_, Bp, ldb_, Mt, Nt, K, threadIdx.x, 256, true);
+    tile_load<T>(As, Bs, Ap, lda_, Bp, ldb_, Mt, Nt, K, threadIdx.x, 256, true, aop);
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -718,8 +743,11 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const void* Am, int lda_
 // that an accumulator register holds 16 consecutive rows of one column.  A
 // zero pivot among the panel's 32 (a zero diagonal entry of U11) leaves its
 // k out, on the VALU, as in the unblocked order.
+// The update covers the columns [c0, c0 + N) of A22 (all M rows), so that
+// the next panel's columns can be updated first and the rest later.
 template <typename T>
-__global__ void __launch_bounds__(256) update_strip_kernel(T* A, int lda, long long sA, int j0, int M, int mstrips)
+__global__ void __launch_bounds__(256) update_strip_kernel(T* A, int lda, long long sA, int j0, int M, int c0, int N,
+                                                           int mstrips)
 {
     using O = ops<T>;
     using R = typename O::R;
@@ -735,9 +763,8 @@ __global__ void __launch_bounds__(256) update_strip_kernel(T* A, int lda, long l
     const int li = lane & 15, lk = lane >> 4;
     T* base = A + mat * sA;
     const T* Lp = base + j0 + NBP + (long long)j0 * lda;             // L21
-    const T* Up = base + j0 + (long long)(j0 + NBP) * lda;           // U12
-    T* Cp = base + j0 + NBP + (long long)(j0 + NBP) * lda;           // A22
-    const int N = M;
+    const T* Up = base + j0 + (long long)(j0 + NBP + c0) * lda;      // U12, columns c0 ..
+    T* Cp = base + j0 + NBP + (long long)(j0 + NBP + c0) * lda;      // A22, columns c0 ..
     const int nct = (N + 63) / 64;
     if (tid == 0) zmask = 0;
     __syncthreads();
@@ -866,7 +893,7 @@ struct CplxStrip {
 
 template <typename R>
 __global__ void __launch_bounds__(256) update_strip_cplx_kernel(cplx<R>* A, int lda, long long sA, int j0, int M,
-                                                                int mstrips)
+                                                                int c0, int N, int mstrips)
 {
     using T = cplx<R>;
     using O = ops<T>;
@@ -885,9 +912,8 @@ __global__ void __launch_bounds__(256) update_strip_cplx_kernel(cplx<R>* A, int 
     const bool hodd = (lk & 1) != 0;                          // this lane's k' = 2k + 1
     T* base = A + mat * sA;
     const T* Lp = base + j0 + NBP + (long long)j0 * lda;             // L21
-    const T* Up = base + j0 + (long long)(j0 + NBP) * lda;           // U12
-    T* Cp = base + j0 + NBP + (long long)(j0 + NBP) * lda;           // A22
-    const int N = M;
+    const T* Up = base + j0 + (long long)(j0 + NBP + c0) * lda;      // U12, columns c0 ..
+    T* Cp = base + j0 + NBP + (long long)(j0 + NBP + c0) * lda;      // A22, columns c0 ..
     const int nct = (N + 63) / 64;
     if (tid == 0) zmask = 0;
     __syncthreads();
@@ -1021,7 +1047,8 @@ template <typename T>
 __global__ void __launch_bounds__(256) gemm_valu_kernel(const void* Am, int lda_, long long sA, const void* Bm,
                                                         int ldb_, long long sB, void* Cm, int ldc, long long sC,
                                                         int M, int N, int K, int mtiles, int ntiles, int kdir,
-                                                        const int* info, const void* Dm, int ldd, long long sD)
+                                                        const int* info, const void* Dm, int ldd, long long sD,
+                                                        int aop)
 {
     using O = ops<T>;
     __shared__ T As[NBP][TT];
@@ -1032,7 +1059,7 @@ __global__ void __launch_bounds__(256) gemm_valu_kernel(const void* Am, int lda_
     const int t = (int)(blockIdx.x % tiles);
     const int i0 = (t % mtiles) * TT, jt0 = (t / mtiles) * TT;
     if (info && info[mat] != 0) return;
-    const T* Ap = (const T*)Am + mat * sA + i0;
+    const T* Ap = (const T*)Am + mat * sA + (aop ? (long long)i0 * lda_ : (long long)i0);
     const T* Bp = (const T*)Bm + mat * sB + (long long)jt0 * ldb_;
     T* Cp = (T*)Cm + mat * sC + i0 + (long long)jt0 * ldc;
     const int Mt = min(TT, M - i0), Nt = min(TT, N - jt0);
@@ -1045,7 +1072,7 @@ __global__ void __launch_bounds__(256) gemm_valu_kernel(const void* Am, int lda_
         const uint64_t zb = __builtin_amdgcn_ballot_w64(z);
         if (threadIdx.x == 0) zmask_s = (unsigned)zb;
     }
-    tile_load<T>(As, Bs, Ap, lda_, Bp, ldb_, Mt, Nt, K, threadIdx.x, 256, false);
+    tile_load<T>(As, Bs, Ap, lda_, Bp, ldb_, Mt, Nt, K, threadIdx.x, 256, false, aop);
     __syncthreads();
     const unsigned zm = zmask_s;
     const int ti = (threadIdx.x % 16) * 4, tj = (threadIdx.x / 16) * 4;
@@ -1138,8 +1165,10 @@ __global__ void __launch_bounds__(1024) left_swap_kernel(Problem p)
 
 // B <- P B: position i receives the row the full interchange sequence brings
 // there (a backward trace of ipiv per row), column by column through LDS.
+// With `reverse`, B <- P^T B: the interchanges applied last to first, so the
+// trace runs forward.
 template <typename T>
-__global__ void __launch_bounds__(1024) permute_rows_kernel(Problem p)
+__global__ void __launch_bounds__(1024) permute_rows_kernel(Problem p, bool reverse)
 {
     extern __shared__ int smem[];
     const int n = p.n;
@@ -1155,7 +1184,8 @@ __global__ void __launch_bounds__(1024) permute_rows_kernel(Problem p)
     __syncthreads();
     for (int i = tid; i < n; i += nt) {
         int x = i;
-        for (int s = n - 1; s >= 0; --s) {
+        for (int q = 0; q < n; ++q) {
+            const int s = reverse ? q : n - 1 - q;
             const int ps = sipiv[s];
             x = (x == s) ? ps : (x == ps ? s : x);
         }
@@ -1223,15 +1253,21 @@ hipError_t launch_panel(const Problem& p, int j0, int w, hipStream_t s) {
 template <typename T>
 hipError_t launch_trsm(const void* Tm, int ldt, long long sT, void* X, int ldx, long long sX, int r0, int w,
                        int ncols, int batch, const int* ipiv, long long sP, bool swap, bool upper,
-                       const int* info, hipStream_t s) {
+                       const int* info, hipStream_t s, bool unit, int aop = 0) {
     const int ct = (ncols + 63) / 64;
     const dim3 grid((unsigned)((long long)ct * batch));
-    if (upper)
-        hipLaunchKernelGGL((trsm_block_kernel<T, true>), grid, dim3(64), 0, s, Tm, ldt, sT, X, ldx, sX, r0, w,
-                           ncols, ct, ipiv, sP, swap, info);
+    if (upper && !unit)
+        hipLaunchKernelGGL((trsm_block_kernel<T, true, false>), grid, dim3(64), 0, s, Tm, ldt, sT, X, ldx, sX, r0,
+                           w, ncols, ct, ipiv, sP, swap, info, aop);
+    else if (upper)
+        hipLaunchKernelGGL((trsm_block_kernel<T, true, true>), grid, dim3(64), 0, s, Tm, ldt, sT, X, ldx, sX, r0,
+                           w, ncols, ct, ipiv, sP, swap, info, aop);
+    else if (unit)
+        hipLaunchKernelGGL((trsm_block_kernel<T, false, true>), grid, dim3(64), 0, s, Tm, ldt, sT, X, ldx, sX, r0,
+                           w, ncols, ct, ipiv, sP, swap, info, aop);
     else
-        hipLaunchKernelGGL((trsm_block_kernel<T, false>), grid, dim3(64), 0, s, Tm, ldt, sT, X, ldx, sX, r0, w,
-                           ncols, ct, ipiv, sP, swap, info);
+        hipLaunchKernelGGL((trsm_block_kernel<T, false, false>), grid, dim3(64), 0, s, Tm, ldt, sT, X, ldx, sX, r0,
+                           w, ncols, ct, ipiv, sP, swap, info, aop);
     return hipGetLastError();
 }
 
@@ -1240,56 +1276,83 @@ hipError_t launch_trsm(const void* Tm, int ldt, long long sT, void* X, int ldx, 
 template <typename T>
 hipError_t launch_gemm(const void* Am, int lda_, long long sA, const void* Bm, int ldb_, long long sB, void* Cm,
                        int ldc, long long sC, int M, int N, int K, int batch, int kdir, const int* info,
-                       hipStream_t s, const void* Dm = nullptr, int ldd = 0, long long sD = 0) {
+                       hipStream_t s, const void* Dm = nullptr, int ldd = 0, long long sD = 0, int aop = 0) {
     if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
     const int mt = (M + TT - 1) / TT, nt = (N + TT - 1) / TT;
     const dim3 grid((unsigned)((long long)mt * nt * batch));
     if constexpr (ops<T>::is_complex)
         hipLaunchKernelGGL((gemm_valu_kernel<T>), grid, dim3(256), 0, s, Am, lda_, sA, Bm, ldb_, sB, Cm, ldc, sC, M,
-                           N, K, mt, nt, kdir, info, Dm, ldd, sD);
+                           N, K, mt, nt, kdir, info, Dm, ldd, sD, aop);
     else
         hipLaunchKernelGGL((gemm_mfma_kernel<T>), grid, dim3(256), 0, s, Am, lda_, sA, Bm, ldb_, sB, Cm, ldc, sC, M,
-                           N, K, mt, nt, kdir, info);
+                           N, K, mt, nt, kdir, info, aop);
     return hipGetLastError();
 }
 
+// U12 = L11^-1 (P A12) for the `rest` columns right of panel j0, displaced
+// rows moved
+template <typename T>
+hipError_t launch_right_solve(const Problem& p, int j0, int rest, hipStream_t s) {
+    T* A = (T*)p.A;
+    if constexpr (sizeof(T) <= 8) {
+        constexpr int TC = StageTile<T>::TC;
+        const int ct = (rest + TC - 1) / TC;
+        hipLaunchKernelGGL((trsm_stage_kernel<T>), dim3((unsigned)((long long)ct * p.batch)), dim3(TC), 0, s, p, j0,
+                           rest, ct);
+        return hipGetLastError();
+    } else {   // complex double: the stage would not fit the registers
+        return launch_trsm<T>(A, p.lda, p.sA, A + (long long)(j0 + NBP) * p.lda, p.lda, p.sA, j0, NBP, rest, p.batch,
+                              p.ipiv, p.sP, true, false, nullptr, s, true);
+    }
+}
+
+// A22 -= L21 U12 on the columns [c0, c0 + N) of the rest x rest trailing matrix
+template <typename T>
+hipError_t launch_update(const Problem& p, int j0, int rest, int c0, int N, hipStream_t s) {
+    T* A = (T*)p.A;
+    if constexpr (!ops<T>::is_complex) {
+        const int ms = (rest + 63) / 64;
+        hipLaunchKernelGGL((update_strip_kernel<T>), dim3((unsigned)((long long)ms * p.batch)), dim3(256), 0, s, A,
+                           p.lda, p.sA, j0, rest, c0, N, ms);
+    } else {
+        using R = typename ops<T>::R;
+        constexpr int SH = CplxStrip<R>::SH;
+        const int ms = (rest + SH - 1) / SH;
+        hipLaunchKernelGGL((update_strip_cplx_kernel<R>), dim3((unsigned)((long long)ms * p.batch)), dim3(256), 0, s,
+                           A, p.lda, p.sA, j0, rest, c0, N, ms);
+    }
+    return hipGetLastError();
+}
+
+// Panel by panel.  With a look-ahead stream, update k covers the next
+// panel's 32 columns first; panel k+1 then runs on the side stream while the
+// rest of update k runs on the caller's stream, and the caller's stream waits
+// for the panel before the next right-hand solve.  The panel writes only its
+// own columns (and ipiv, info) and the remaining update only the columns
+// beyond them, so the two touch disjoint data; every element still takes its
+// updates in the same order.
 template <typename T>
 hipError_t getrf_t(const Problem& p, hipStream_t s) {
     const int n = p.n;
     hipError_t e;
-    for (int j0 = 0; j0 < n; j0 += NBP) {
-        const int w = min(NBP, n - j0);
-        if ((e = launch_panel<T>(p, j0, w, s)) != hipSuccess) return e;
-        const int rest = n - j0 - w;
-        if (rest <= 0) break;
-        T* A = (T*)p.A;
-        // U12 = L11^-1 * (P A12), displaced rows moved (w == NBP: a trailing
-        // matrix exists)
-        if constexpr (sizeof(T) <= 8) {
-            constexpr int TC = StageTile<T>::TC;
-            const int ct = (rest + TC - 1) / TC;
-            hipLaunchKernelGGL((trsm_stage_kernel<T>), dim3((unsigned)((long long)ct * p.batch)), dim3(TC), 0, s, p,
-                               j0, rest, ct);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        } else {   // complex double: the stage would not fit the registers
-            if ((e = launch_trsm<T>(A, p.lda, p.sA, A + (long long)(j0 + w) * p.lda, p.lda, p.sA, j0, w, rest,
-                                    p.batch, p.ipiv, p.sP, true, false, nullptr, s)) != hipSuccess)
-                return e;
+    LookAhead la;
+    const bool ahead = n > 2 * NBP && lookahead_begin(la);
+    if ((e = launch_panel<T>(p, 0, min(NBP, n), s)) != hipSuccess) return lookahead_end(la, e);
+    for (int j0 = 0; j0 + NBP < n; j0 += NBP) {
+        const int rest = n - j0 - NBP;
+        const int nw = min(NBP, rest);          // width of the next panel
+        if ((e = launch_right_solve<T>(p, j0, rest, s)) != hipSuccess) return lookahead_end(la, e);
+        if (!ahead || rest == nw) {
+            if ((e = launch_update<T>(p, j0, rest, 0, rest, s)) != hipSuccess) return lookahead_end(la, e);
+            if ((e = launch_panel<T>(p, j0 + NBP, nw, s)) != hipSuccess) return lookahead_end(la, e);
+            continue;
         }
-        // A22 -= L21 * U12
-        if constexpr (!ops<T>::is_complex) {
-            const int ms = (rest + 63) / 64;
-            hipLaunchKernelGGL((update_strip_kernel<T>), dim3((unsigned)((long long)ms * p.batch)), dim3(256), 0, s,
-                               A, p.lda, p.sA, j0, rest, ms);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        } else {
-            using R = typename ops<T>::R;
-            constexpr int SH = CplxStrip<R>::SH;
-            const int ms = (rest + SH - 1) / SH;
-            hipLaunchKernelGGL((update_strip_cplx_kernel<R>), dim3((unsigned)((long long)ms * p.batch)), dim3(256), 0,
-                               s, A, p.lda, p.sA, j0, rest, ms);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
+        if ((e = launch_update<T>(p, j0, rest, 0, nw, s)) != hipSuccess) return lookahead_end(la, e);
+        if ((e = lookahead_fork(la, s)) != hipSuccess) return lookahead_end(la, e);
+        if ((e = launch_panel<T>(p, j0 + NBP, nw, la.side)) != hipSuccess) return lookahead_end(la, e);
+        if ((e = lookahead_join_record(la)) != hipSuccess) return lookahead_end(la, e);
+        if ((e = launch_update<T>(p, j0, rest, nw, rest - nw, s)) != hipSuccess) return lookahead_end(la, e);
+        if ((e = lookahead_join_wait(la, s)) != hipSuccess) return lookahead_end(la, e);
     }
     if (n > NBP) {
         const int nt = panel_threads(n);
@@ -1298,49 +1361,92 @@ hipError_t getrf_t(const Problem& p, hipStream_t s) {
         if (rpt <= 1) hipLaunchKernelGGL((left_swap_kernel<T, 1>), dim3(p.batch), dim3(nt), smem, s, p);
         else if (rpt <= 2) hipLaunchKernelGGL((left_swap_kernel<T, 2>), dim3(p.batch), dim3(nt), smem, s, p);
         else if (rpt <= 4) hipLaunchKernelGGL((left_swap_kernel<T, 4>), dim3(p.batch), dim3(nt), smem, s, p);
-        else return hipErrorInvalidValue;
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        else return lookahead_end(la, hipErrorInvalidValue);
+        if ((e = hipGetLastError()) != hipSuccess) return lookahead_end(la, e);
     }
-    return hipSuccess;
+    return lookahead_end(la, hipSuccess);
 }
 
 template <typename T>
+hipError_t launch_permute(const Problem& p, bool reverse, hipStream_t s) {
+    const int nt = panel_threads(p.n);
+    const size_t smem = (size_t)2 * p.n * sizeof(int) + 16 + (size_t)p.n * sizeof(T);
+    hipLaunchKernelGGL((permute_rows_kernel<T>), dim3(p.batch), dim3(nt), smem, s, p, reverse);
+    return hipGetLastError();
+}
+
+// Solve with the factors block row by block row: a 32-row triangular-block
+// solve, then a GEMM update of the rows still to come, which takes each k of
+// the block in substitution order, so every element of X sees the
+// substitutions' operation sequence.
+//   A X = B:   B <- P B; L Y = B, blocks ascending; U X = Y, blocks descending.
+//   A^T X = B, A^H X = B (op = T or H, conjugated factors for H):
+//              op(U) W = B, blocks ascending, dividing by the diagonal;
+//              op(L) Z = W, blocks descending, unit diagonal; X = P^T Z.
+// The block of op(L) or op(U) at rows [i0, ..) and columns [k0, ..) is read
+// transposed from the stored factor at rows [k0, ..), columns [i0, ..).
+template <typename T>
 hipError_t getrs_t(const Problem& p, hipStream_t s) {
-    const int n = p.n, nrhs = p.nrhs;
+    const int n = p.n, nrhs = p.nrhs, aop = p.trans;
+    const long long lda = p.lda;
     hipError_t e;
-    {
-        const int nt = panel_threads(n);
-        const size_t smem = (size_t)2 * n * sizeof(int) + 16 + (size_t)n * sizeof(T);
-        hipLaunchKernelGGL((permute_rows_kernel<T>), dim3(p.batch), dim3(nt), smem, s, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    if (aop == 0 && (e = launch_permute<T>(p, false, s)) != hipSuccess) return e;
     const T* A = (const T*)p.A;
     T* B = (T*)p.B;
-    // forward: L Y = P B, block rows ascending
+    // forward: L Y = P B or op(U) W = B, block rows ascending
     for (int r0 = 0; r0 < n; r0 += NBP) {
         const int w = min(NBP, n - r0);
         if ((e = launch_trsm<T>(A, p.lda, p.sA, B, p.ldb, p.sB, r0, w, nrhs, p.batch, nullptr, 0, false, false,
-                                p.info, s)) != hipSuccess)
+                                p.info, s, aop == 0, aop)) != hipSuccess)
             return e;
         const int rest = n - r0 - w;
-        if (rest > 0 &&
-            (e = launch_gemm<T>(A + r0 + w + (long long)r0 * p.lda, p.lda, p.sA, B + r0, p.ldb, p.sB, B + r0 + w,
-                                p.ldb, p.sB, rest, nrhs, w, p.batch, 1, p.info, s)) != hipSuccess)
+        if (rest <= 0) continue;
+        const T* blk = aop ? A + r0 + (r0 + w) * lda : A + r0 + w + r0 * lda;
+        if ((e = launch_gemm<T>(blk, p.lda, p.sA, B + r0, p.ldb, p.sB, B + r0 + w, p.ldb, p.sB, rest, nrhs, w,
+                                p.batch, 1, p.info, s, nullptr, 0, 0, aop)) != hipSuccess)
             return e;
     }
-    // back: U X = Y, block rows descending
+    // back: U X = Y or op(L) Z = W, block rows descending
     const int last = ((n - 1) / NBP) * NBP;
     for (int r0 = last; r0 >= 0; r0 -= NBP) {
         const int w = min(NBP, n - r0);
         if ((e = launch_trsm<T>(A, p.lda, p.sA, B, p.ldb, p.sB, r0, w, nrhs, p.batch, nullptr, 0, false, true,
-                                p.info, s)) != hipSuccess)
+                                p.info, s, aop != 0, aop)) != hipSuccess)
             return e;
-        if (r0 > 0 &&
-            (e = launch_gemm<T>(A + (long long)r0 * p.lda, p.lda, p.sA, B + r0, p.ldb, p.sB, B, p.ldb, p.sB, r0,
-                                nrhs, w, p.batch, -1, p.info, s)) != hipSuccess)
+        if (r0 == 0) continue;
+        const T* blk = aop ? A + r0 : A + r0 * lda;
+        if ((e = launch_gemm<T>(blk, p.lda, p.sA, B + r0, p.ldb, p.sB, B, p.ldb, p.sB, r0, nrhs, w, p.batch, -1,
+                                p.info, s, nullptr, 0, 0, aop)) != hipSuccess)
             return e;
     }
+    if (aop != 0 && (e = launch_permute<T>(p, true, s)) != hipSuccess) return e;
     return hipSuccess;
+}
+
+// C = I, one work-group per (column, matrix)
+template <typename T>
+__global__ void __launch_bounds__(256) identity_kernel(T* C, int ldc, long long sC, int n)
+{
+    using O = ops<T>;
+    const int j = (int)(blockIdx.x % (unsigned)n);
+    const long long mat = blockIdx.x / (unsigned)n;
+    T* col = C + mat * sC + (long long)j * ldc;
+    for (int i = threadIdx.x; i < n; i += 256) col[i] = i == j ? O::one() : O::zero();
+}
+
+// getri above the one-launch solve's order: C = I, then the blocked NoTrans
+// solve on it
+template <typename T>
+hipError_t getri_t(const Problem& p, hipStream_t s) {
+    hipLaunchKernelGGL((identity_kernel<T>), dim3((unsigned)((long long)p.n * p.batch)), dim3(256), 0, s, (T*)p.B,
+                       p.ldb, p.sB, p.n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    Problem q = p;
+    q.nrhs = p.n;
+    q.trans = 0;
+    q.info = nullptr;
+    return getrs_t<T>(q, s);
 }
 
 }  // namespace

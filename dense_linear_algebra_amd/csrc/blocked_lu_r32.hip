@@ -6,5 +6,6 @@ namespace batchlu {
 
 hipError_t blocked_getrf_r32(const Problem& p, hipStream_t s) { return getrf_t<float>(p, s); }
 hipError_t blocked_getrs_r32(const Problem& p, hipStream_t s) { return getrs_t<float>(p, s); }
+hipError_t blocked_getri_r32(const Problem& p, hipStream_t s) { return getri_t<float>(p, s); }
 
 }  // namespace batchlu

@@ -6,5 +6,6 @@ namespace batchlu {
 
 hipError_t blocked_getrf_r64(const Problem& p, hipStream_t s) { return getrf_t<double>(p, s); }
 hipError_t blocked_getrs_r64(const Problem& p, hipStream_t s) { return getrs_t<double>(p, s); }
+hipError_t blocked_getri_r64(const Problem& p, hipStream_t s) { return getri_t<double>(p, s); }
 
 }  // namespace batchlu

@@ -45,8 +45,28 @@ hipError_t cta_lds_launch(int dtype, const Problem& p, int mode, hipStream_t s);
 bool blocked_fused_supported(int dtype, int n, int lda);
 hipError_t blocked_fused_getrf(int dtype, const Problem& p, hipStream_t s);
 
+// A second stream on the current device for running a panel beside the
+// previous panel's trailing update, with the two events of the fork and the
+// join.  Created once per device; lookahead_begin also takes a lock held
+// until lookahead_end, so that concurrent callers do not interleave their
+// event records.  lookahead_begin returns false (and the caller runs without
+// look-ahead) if the stream or events cannot be created.
+struct LookAhead {
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool held = false;
+};
+bool lookahead_begin(LookAhead& la);
+hipError_t lookahead_fork(LookAhead& la, hipStream_t s);       // side waits for s's work so far
+hipError_t lookahead_join_record(LookAhead& la);               // marks the side's work so far
+hipError_t lookahead_join_wait(LookAhead& la, hipStream_t s);  // s waits for that mark
+hipError_t lookahead_end(LookAhead& la, hipError_t status);    // releases the lock, returns status
+
 // Blocked right-looking tier (panel, laswp, trsm, gemm) and blocked getrs.
+// blocked_getrs serves every p.trans and, with p.inverse, getri (B is the
+// output C, set to the identity first); n <= 4096.
 bool blocked_supported(int dtype, int n);
+bool blocked_getrs_supported(int dtype, int n);
 hipError_t blocked_getrf(int dtype, const Problem& p, hipStream_t s);
 hipError_t blocked_getrs(int dtype, const Problem& p, hipStream_t s);
 

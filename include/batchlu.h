@@ -50,7 +50,7 @@ typedef enum {
 
 /* status codes (negative values -1 .. -20 name an invalid argument) */
 #define BATCHLU_OK 0
-#define BATCHLU_ERR_UNSUPPORTED (-100) /* e.g. getrs 'T'/'C' with n > 1024     */
+#define BATCHLU_ERR_UNSUPPORTED (-100) /* e.g. getrs or getri with n > 4096    */
 #define BATCHLU_ERR_CAPACITY (-101)    /* no tier can run this shape           */
 #define BATCHLU_ERR_LAUNCH (-102)      /* a kernel launch failed (HIP error)   */
 
@@ -84,8 +84,9 @@ int batchlu_getrf(batchlu_dtype t, int n, void* A, int lda, long long strideA,
 /*
  * batchlu_getrs -- solve op(A) X = B with the factors and ipiv of batchlu_getrf.
  *   1 t, 2 trans: 'N' solves A X = B, 'T' A^T X = B, 'C' A^H X = B (A^T
- *     for real types); 'T'/'C' need n <= 1024, else BATCHLU_ERR_UNSUPPORTED,
- *   3 n, 4 nrhs >= 0, 5 A (device, read only), 6 lda, 7 strideA,
+ *     for real types),
+ *   3 n (<= 4096, else BATCHLU_ERR_UNSUPPORTED: one launch solves n <= 1024,
+ *     larger n runs block row by block row), 4 nrhs >= 0, 5 A (device, read only), 6 lda, 7 strideA,
  *   8 ipiv (device, read only; an entry outside 1..n is read as "no
  *     interchange" so that a corrupt list cannot address rows outside B),
  *   9 strideP,
@@ -119,7 +120,7 @@ int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda,
 /*
  * batchlu_getri -- C = A^{-1} from the factors and ipiv of batchlu_getrf,
  * out of place.
- *   1 t, 2 n (0 <= n <= 1024; larger n returns BATCHLU_ERR_UNSUPPORTED),
+ *   1 t, 2 n (0 <= n <= 4096; larger n returns BATCHLU_ERR_UNSUPPORTED),
  *   3 A (device, read only: the factors), 4 lda >= max(1, n),
  *   5 strideA >= lda*n when batch > 1,
  *   6 ipiv (device, read only; an entry outside 1..n is read as "no
@@ -133,7 +134,8 @@ int batchlu_gesv(batchlu_dtype t, int n, int nrhs, void* A, int lda,
  * and the section on the shared interchange kernels (the pivoting is undone
  * inside the solve, with no separate permutation pass): computed as the
  * NoTrans solve of A C = I, whose right-hand sides are formed in registers
- * and never stored.
+ * and never stored (n <= 1024), or, for larger n, C set to the identity and
+ * then solved in place block row by block row.
  */
 int batchlu_getri(batchlu_dtype t, int n, const void* A, int lda,
                   long long strideA, const int* ipiv, long long strideP,

@@ -244,3 +244,21 @@ def dominant_spd_problem(seed: int, dtype, n: int, nrhs: int, batch: int):
     A = np.ascontiguousarray(np.swapaxes(M, 1, 2)).reshape(-1).astype(dt)
     B = draw(rng, dt, batch * n * nrhs)
     return A, B
+
+
+def packed_factors(seed: int, dtype, n: int, batch: int):
+    """Stand-in LU factors for solve-only tests at orders where factoring on
+    the host would take long: packed unit-lower L and upper U (column-major,
+    stride n*n) with off-diagonal entries uniform in [-1, 1] / n and U's
+    diagonal 1 + uniform[0, 1) (so every solve stays well scaled), and a
+    1-based interchange list with entry k drawn from k+1 .. n."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    LU = draw(rng, dtype, batch * n * n) / np.dtype(dtype).type(n)
+    d = 1.0 + rng.random((batch, n))
+    v = LU.reshape(batch, n, n)        # [b, column, row]
+    for b in range(batch):
+        v[b][np.arange(n), np.arange(n)] = d[b]
+    ipiv = np.empty((batch, n), np.int32)
+    for k in range(n):
+        ipiv[:, k] = rng.integers(k, n, size=batch) + 1
+    return LU, ipiv

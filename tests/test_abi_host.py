@@ -59,8 +59,8 @@ def test_getrf_argument_checks(args, expect):
     ((0, "X", 4, 1, FAKE, 4, 16, FAKE, 4, FAKE, 4, 4, 1), -2),    # bad trans
     ((0, "N", 4, -1, FAKE, 4, 16, FAKE, 4, FAKE, 4, 4, 1), -4),   # nrhs < 0
     ((0, "N", 4, 2, FAKE, 4, 16, FAKE, 4, FAKE, 4, 7, 2), -12),   # strideB < ldb*nrhs
-    ((0, "T", 2000, 1, FAKE, 2000, 4000000, FAKE, 2000, FAKE, 2000, 2000, 1), -100),  # 'T' above n = 1024
-    ((3, "C", 1025, 2, FAKE, 1025, 1050625, FAKE, 1025, FAKE, 1025, 2050, 1), -100),  # 'C' above n = 1024
+    ((0, "T", 5000, 1, FAKE, 5000, 25000000, FAKE, 5000, FAKE, 5000, 5000, 1), -100),  # 'T' above n = 4096
+    ((3, "C", 4097, 2, FAKE, 4097, 16785409, FAKE, 4097, FAKE, 4097, 8194, 1), -100),  # 'C' above n = 4096
     ((0, "T", 0, 1, None, 1, 0, None, 0, None, 1, 1, 3), 0),      # 'T' with n == 0: no work
     ((0, "N", 4, 0, None, 4, 16, None, 4, None, 4, 0, 3), 0),     # nrhs == 0
 ])
@@ -76,7 +76,7 @@ def test_getrs_argument_checks(args, expect):
     ((0, 4, FAKE, 4, 16, None, 4, FAKE + 4096, 4, 16, 1), -6),    # ipiv null
     ((0, 4, FAKE, 4, 16, FAKE, 4, FAKE + 60, 4, 16, 1), -8),      # C overlaps A's last element
     ((0, 4, FAKE, 4, 16, FAKE, 4, FAKE, 4, 16, -1), -11),         # batch < 0
-    ((0, 1100, FAKE, 1100, 1210000, FAKE, 1100, 1 << 40, 1100, 1210000, 1), -100),  # n > 1024
+    ((0, 4100, FAKE, 4100, 16810000, FAKE, 4100, 1 << 40, 4100, 16810000, 1), -100),  # n > 4096
     ((0, 0, None, 1, 0, None, 0, None, 1, 0, 5), 0),              # n == 0: no work
 ])
 def test_getri_argument_checks(args, expect):

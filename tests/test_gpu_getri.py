@@ -4,7 +4,8 @@ the oracle's getri on the same factors, through the C ABI.
 Bar: C bit-identical (the kernel runs the NoTrans solve on the identity in
 the oracle's order), plus the residual of A C = I.  Edge cases: n = 1,
 block and wavefront boundaries, ragged column tiles, n = 1024 (factors from
-the oracle, so only the inverse runs on the GPU), padded ldc and strides
+the oracle, so only the inverse runs on the GPU), orders above 1024 (the
+identity, then the block-row-by-block-row solve), padded ldc and strides
 with the pads untouched."""
 import numpy as np
 import pytest
@@ -95,3 +96,24 @@ def test_getri_padded_layout(dtype):
         for c in range(n):
             pad[b * sC + c * ldc: b * sC + c * ldc + n] = False
     np.testing.assert_array_equal(bits(gC[pad]), bits(C0[pad]))
+
+
+@pytest.mark.parametrize("dtype,n", [(np.float64, 1100), (np.complex64, 1057), (np.float32, 1500)],
+                         ids=lambda v: getattr(v, "__name__", str(v)))
+def test_getri_blocked_orders(dtype, n):
+    """Above n = 1024: C set to the identity, then solved in place block row
+    by block row.  Synthetic packed factors; C bitwise against the oracle's
+    getri (padded ldc, pads untouched)."""
+    batch, ldc = 1, n + 3
+    LU, ipiv = lu_inputs.packed_factors(9800 + n, dtype, n, batch)
+    print(f"case blocked getri dtype={np.dtype(dtype).name} n={n}", flush=True)
+    C0 = np.full(ldc * n, -5.5, dtype)
+    gC = _getri_gpu(LU, ipiv, C0, n, batch, n, n * n, ldc, ldc * n, n)
+    oC = np.zeros(n * n, dtype)
+    oracle.getri(LU, n, n, n * n, ipiv, oC, n, n * n, batch)
+    dense = lu_inputs.relayout(gC, n, n, batch, ldc, ldc * n, n, n * n)
+    assert matrices_equal_bits(dense, oC, n, n, n, n * n, batch) == []
+    pad = np.ones(ldc * n, bool)
+    for c in range(n):
+        pad[c * ldc: c * ldc + n] = False
+    assert (gC[pad] == dtype(-5.5)).all()

@@ -6,9 +6,10 @@ factors, so the comparison isolates the solve.  Bar: X bit-identical (the
 kernel accumulates each element in the oracle's order: ascending k against
 U^T with true division by u_kk, descending k against L^T), plus the solve
 residual of op(A) X = B for well-conditioned inputs.  Edge cases: n = 1,
-block and wavefront boundaries, the n = 1024 limit, ragged right-hand-side
-tiles, padded leading dimensions and batch strides (pads untouched), and
-n > 1024, which must be refused."""
+block and wavefront boundaries, n = 1024 (the one-launch solve's largest
+order), the block-row-by-block-row solve above it up to n = 4096 (also for
+'N'), ragged right-hand-side tiles, padded leading dimensions and batch
+strides (pads untouched), and n > 4096, which must be refused."""
 import numpy as np
 import pytest
 
@@ -111,8 +112,48 @@ def test_getrs_trans_padded_layout(dtype):
     np.testing.assert_array_equal(bits(gB[pad]), bits(Bp[pad]))
 
 
+BLOCKED = [(np.float32, 1025, "T"), (np.float32, 1100, "N"), (np.float64, 1057, "T"), (np.complex64, 1030, "C"),
+           (np.complex64, 1030, "T"), (np.complex128, 1090, "C"), (np.float64, 2048, "N"), (np.float32, 4096, "T"),
+           (np.complex64, 4096, "C")]
+
+
+@pytest.mark.parametrize("dtype,n,trans", BLOCKED, ids=lambda v: getattr(v, "__name__", str(v)))
+def test_getrs_blocked_orders_match_oracle_bitwise(dtype, n, trans):
+    """Above n = 1024 the solve runs block row by block row: a 32-row
+    triangular solve, then a GEMM update (transposed and, for 'C',
+    conjugated reads of the factor for op(A) = A^T, A^H).  Synthetic packed
+    factors and interchanges; X bitwise against the oracle's solve."""
+    nrhs, batch = 3, 1 if n > 2048 else 2
+    LU, ipiv = lu_inputs.packed_factors(9500 + n, dtype, n, batch)
+    _, B = lu_inputs.random_problem(9600 + n, dtype, n, nrhs, batch)
+    print(f"case blocked getrs trans={trans} dtype={np.dtype(dtype).name} n={n} nrhs={nrhs}", flush=True)
+    gB = _getrs_gpu(LU, ipiv, B, n, nrhs, batch, trans, n, n * n, n, n * nrhs, n)
+    oB = B.copy()
+    oracle.getrs(LU, n, n, n * n, ipiv, oB, nrhs, n, n * nrhs, batch, trans=trans)
+    assert np.isfinite(oB).all()
+    assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
+
+
+def test_getrs_trans_blocked_from_gpu_factors():
+    """n = 1100 float factored on the GPU (blocked tier), solved with A^T
+    above the one-launch order: bitwise against the oracle's solve with the
+    same factors, and a small residual of A^T X = B."""
+    dtype, n, nrhs, batch = np.float32, 1100, 4, 1
+    A, B = lu_inputs.random_problem(9700, dtype, n, nrhs, batch)
+    print(f"case blocked getrs trans=T from GPU factors n={n}", flush=True)
+    gA, _, gP, gI = gesv_gpu(lib, A, None, n, 0, batch, op="getrf")
+    assert np.all(gI == 0)
+    gB = _getrs_gpu(gA, gP[:, :n], B, n, nrhs, batch, "T", n, n * n, n, n * nrhs, n)
+    oB = B.copy()
+    oracle.getrs(gA, n, n, n * n, gP[:, :n], oB, nrhs, n, n * nrhs, batch, trans="T")
+    assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
+    Am = oracle.matrix(A, 0, n, n, n, n * n)
+    assert oracle.solve_residual(Am.T, oracle.matrix(gB, 0, n, nrhs, n, n * nrhs),
+                                 oracle.matrix(B, 0, n, nrhs, n, n * nrhs)) <= 20
+
+
 def test_getrs_trans_above_limit_is_refused():
-    n = 1100
+    n = 4097
     dA = torch.zeros(n * n, dtype=torch.float32, device="cuda")
     dB = torch.zeros(n, dtype=torch.float32, device="cuda")
     dP = torch.ones(n, dtype=torch.int32, device="cuda")
