@@ -19,8 +19,9 @@
 //   - For gesv the right-hand sides ride along as extra columns of the rank-1
 //     update (the forward solve).  The back substitution multiplies by the
 //     reciprocal of each diagonal entry, computed once at its elimination
-//     step (BatchLAS "Blackwell" page, getrs tiny paragraph); X is staged in
-//     LDS and stored with row-contiguous vector writes.
+//     step (BatchLAS "Blackwell" page, getrs tiny paragraph); each entry of
+//     x_k is formed by one lane and staged in LDS, where the rows above read
+//     it back, and X leaves from the stage with row-contiguous vector writes.
 // Arithmetic per element is the same operation sequence as the unblocked
 // right-looking LU, so L, U and ipiv are bit-identical to it.
 #pragma once
@@ -317,12 +318,14 @@ register_lu_kernel(Problem p, int mode)
     }
 
     // ---- back substitution U x = y (gesv) ---------------------------------
-    // Step k: the row at position k publishes y_k, every lane forms
-    // x_k = y_k * (1/u_kk) (or y_k / u_kk when u_kk is below the smallest
-    // normal), lane 0 of the group stages x_k, and the rows above position k
-    // subtract u_ik * x_k.
+    // Step k: the row at position k publishes y_k; lane r of the group forms
+    // x_kr = y_kr * (1/u_kk) (or y_kr / u_kk when u_kk is below the smallest
+    // normal) for right-hand sides r = li, li + LPM, ..., and stages it; then
+    // every row above position k reads x_k back and subtracts u_ik * x_k.
+    // Each x_kr is formed once instead of in every lane of the group.
     if constexpr (NR > 0) {
         if (solve) {
+            const T* const ybuf = reinterpret_cast<const T*>(&rowbuf[grp][0]);
 #pragma unroll
             for (int k = NB - 1; k >= 0; --k) {
                 if (k >= n) continue;
@@ -340,30 +343,33 @@ register_lu_kernel(Problem p, int mode)
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                {
+                    const T rk = diag[2 * k];
+                    const T dk = diag[2 * k + 1];
+                    const bool tiny = !(O::metric(dk) >= O::sfmin());
+                    T* const xs = reinterpret_cast<T*>(&xstage[grp][k * NRC]);
+#pragma unroll
+                    for (int r0 = 0; r0 < NR; r0 += LPM) {
+                        const int r2 = r0 + li;
+                        if (r2 < NR) {
+                            const T y = ybuf[r2];
+                            T x = O::mul(y, rk);
+                            if (__builtin_expect(__builtin_amdgcn_ballot_w64(tiny) != 0, 0)) {
+                                asm volatile("" ::: "memory");
+                                if (tiny) x = O::div(y, dk);
+                            }
+                            xs[r2] = x;
+                        }
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 T xk[NRP];
 #pragma unroll
                 for (int c = 0; c < NRC; ++c) {
-                    uint4 w = rowbuf[grp][c];
+                    uint4 w = xstage[grp][k * NRC + c];
                     __builtin_memcpy(&xk[c * CH], &w, 16);
-                }
-                const T rk = diag[2 * k];
-                const T dk = diag[2 * k + 1];
-                const bool tiny = !(O::metric(dk) >= O::sfmin());
-                if (__builtin_expect(__builtin_amdgcn_ballot_w64(tiny) != 0, 0)) {
-                    asm volatile("" ::: "memory");
-#pragma unroll
-                    for (int r2 = 0; r2 < NR; ++r2) xk[r2] = tiny ? O::div(xk[r2], dk) : O::mul(xk[r2], rk);
-                } else {
-#pragma unroll
-                    for (int r2 = 0; r2 < NR; ++r2) xk[r2] = O::mul(xk[r2], rk);
-                }
-                if (li == 0) {
-#pragma unroll
-                    for (int c = 0; c < NRC; ++c) {
-                        uint4 w;
-                        __builtin_memcpy(&w, &xk[c * CH], 16);
-                        xstage[grp][k * NRC + c] = w;
-                    }
                 }
 #pragma unroll
                 for (int s = 0; s < RPL; ++s) {
@@ -372,9 +378,6 @@ register_lu_kernel(Problem p, int mode)
                         for (int r2 = 0; r2 < NR; ++r2) O::fms(b[s][r2], a[s][k], xk[r2]);
                     }
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
         }
     }

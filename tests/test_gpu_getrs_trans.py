@@ -114,7 +114,7 @@ def test_getrs_trans_padded_layout(dtype):
 
 BLOCKED = [(np.float32, 1025, "T"), (np.float32, 1100, "N"), (np.float64, 1057, "T"), (np.complex64, 1030, "C"),
            (np.complex64, 1030, "T"), (np.complex128, 1090, "C"), (np.float64, 2048, "N"), (np.float32, 4096, "T"),
-           (np.complex64, 4096, "C")]
+           (np.complex64, 4096, "C"), (np.float64, 4096, "C"), (np.complex128, 4096, "T")]
 
 
 @pytest.mark.parametrize("dtype,n,trans", BLOCKED, ids=lambda v: getattr(v, "__name__", str(v)))
