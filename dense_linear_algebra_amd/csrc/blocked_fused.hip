@@ -43,11 +43,11 @@ namespace {
 constexpr int NB = 32;        // panel width
 constexpr int NT = 256;       // threads per work-group = largest order
 constexpr int NW = NT / 64;   // wavefronts
-// LDS stage for U12: CW trailing columns at a time (the widest trailing
-// matrix at once; a narrower stage lets more f64 work-groups share a compute
-// unit's LDS, but their registers already limit them to two)
-template <typename T> struct Stage {
-    static constexpr int CW = NT - NB;
+// LDS stage for U12: CW trailing columns at a time.  The widest trailing
+// matrix at once where LDS allows; f64 budgeted for three work-groups per
+// compute unit stages 112 columns (three 43 KB work-groups fit the 160 KB).
+template <typename T, int WPE> struct Stage {
+    static constexpr int CW = (sizeof(T) == 8 && WPE >= 3) ? 112 : NT - NB;
     static constexpr int SLD = CW + 8;   // padded against bank conflicts
 };
 
@@ -84,7 +84,8 @@ __device__ inline int mfma_row(int lk, int r) {
 }
 
 // WPE: wavefronts per SIMD the registers are budgeted for (= work-groups per
-// compute unit: f32 4; f64 2, which its LDS stage allows as well)
+// compute unit: f32 4; f64 2 with the full-width stage, or 3 with the
+// 112-column stage: 168 VGPRs, no spill)
 template <typename T, int WPE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
 lu_fused_kernel(Problem p, uint32_t extent_bytes)
@@ -103,7 +104,7 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
     __shared__ int src_top[NB], src_low[NB], dst_low[NB];
     __shared__ int nlow;
     __shared__ int csrc[NT];                  // trailing position -> row holding it (relative to j0)
-    constexpr int CW = Stage<T>::CW, SLD = Stage<T>::SLD;
+    constexpr int CW = Stage<T, WPE>::CW, SLD = Stage<T, WPE>::SLD;
     __shared__ T S[NB][SLD];                  // P A12, then U12 (rows of the panel x trailing columns)
 
     const int n = p.n;
@@ -467,7 +468,14 @@ hipError_t blocked_fused_getrf(int dtype, const Problem& p, hipStream_t s) {
     const uint32_t ext = (uint32_t)extent_of(dtype, p.n, p.lda);
     if (dtype == R32)
         hipLaunchKernelGGL((lu_fused_kernel<float, 4>), dim3((unsigned)p.batch), dim3(NT), 0, s, p, ext);
+    else if (p.n <= 224 || p.batch > 1024)
+        // three work-groups per compute unit: measured 3 - 23 % faster (n = 96 -
+        // 224 at batch 1024 - 4096, n = 256 above batch 1024)
+        hipLaunchKernelGGL((lu_fused_kernel<double, 3>), dim3((unsigned)p.batch), dim3(NT), 0, s, p, ext);
     else
+        // n = 256 at batch <= 1024: two work-groups per compute unit with the
+        // full-width stage (three per unit leave a partial second round
+        // there; measured 2 % slower)
         hipLaunchKernelGGL((lu_fused_kernel<double, 2>), dim3((unsigned)p.batch), dim3(NT), 0, s, p, ext);
     return hipGetLastError();
 }

@@ -179,3 +179,22 @@ def test_blocked_full_size_workloads(name):
         sr = oracle.solve_residual(Am, oracle.matrix(gB, b, w.n, w.nrhs, w.n, w.n * w.nrhs),
                                    oracle.matrix(B, b, w.n, w.nrhs, w.n, w.n * w.nrhs))
         assert sr <= 20, f"matrix {b}: solve residual {sr}"
+
+
+@pytest.mark.parametrize("n,batch", [(256, 1100), (200, 700)])
+def test_fused_double_three_per_compute_unit(n, batch):
+    """The double one-work-group kernel budgeted for three work-groups per
+    compute unit (112-column U12 stage: several stage chunks per panel),
+    which serves n <= 224 and batches above 1024: ipiv, info and LU
+    bit-identical to the oracle on matrices spread over the batch."""
+    dtype = np.float64
+    A, _ = lu_inputs.random_problem(4400 + n, dtype, n, 1, batch)
+    print(f"case fused f64 3/CU n={n} batch={batch}", flush=True)
+    gA, _, gP, gI = gesv_gpu(lib, A, None, n, 0, batch, op="getrf")
+    for b in np.linspace(0, batch - 1, 4).astype(int):
+        sl = slice(b * n * n, (b + 1) * n * n)
+        oA = A[sl].copy()
+        oP, oI, _, _ = oracle.getrf(oA, n, n, n * n, 1)
+        assert gI[b] == oI[0]
+        np.testing.assert_array_equal(gP[b, :n], oP[0])
+        assert np.array_equal(bits(gA[sl]), bits(oA))
