@@ -234,13 +234,17 @@ __device__ inline int group_min(int v) {
 // wavefront argmax and an LDS-only work-group barrier (blocked-tier panels)
 // ---------------------------------------------------------------------------
 // maximum over the wavefront, returned wave-uniform: DPP inside each row of
-// 16 lanes, then the four row results by readlane
+// 16 lanes, then across the rows
 __device__ inline uint32_t wave_max(uint32_t v) {
     v = group_max<16>(v);
-    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-    const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
-    return a > b ? a : b;
+    // row_bcast:15 hands each even row's maximum to the next row (rows 1 and
+    // 3), row_bcast:31 row 1's to rows 2 and 3; lane 63 then holds the
+    // wavefront's maximum (disabled rows keep the identity 0 as the operand)
+    uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+    v = o > v ? o : v;
+    o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+    v = o > v ? o : v;
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 // 64-bit keys: the high words first, then the low words among the lanes
 // that hold the maximal high word
