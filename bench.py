@@ -136,7 +136,7 @@ def write_counter_summary(workload: str, kernel: str, fetch_db: str, write_db: s
     copy_mb MiB that the same run made first (bench.py --copy-probe-mb).
     For a workload whose step is several launches, `kernel` is the dominant
     one and the bytes are per launch of it."""
-    w = lu_inputs.WORKLOADS[workload]
+    w = ALL_WORKLOADS[workload]
     res = {"kernel": kernel, "workload": workload, "source_hash": source_hash(workload), "commands": list(commands)}
     # several kernels may be named, separated by '|': their bytes are summed
     # and divided by the dispatches of the first one (e.g. the launches of one
