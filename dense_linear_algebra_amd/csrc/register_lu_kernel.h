@@ -54,6 +54,9 @@ constexpr bool reg_chunked() { return NB * (int)sizeof(T) >= 512; }
 template <typename T, int NB, int NR>
 constexpr int reg_waves() {
     if (!reg_chunked<T, NB>()) return 1;
+    // one matrix per wavefront with its one right-hand side in LDS: three,
+    // as without B
+    if (NR == 1 && NB == 64 && sizeof(T) == 8) return 3;
     if (sizeof(T) == 8) return (ops<T>::is_complex || NR <= 8) ? 2 : 1;
     return NR <= 1 ? 2 : 1;
 }
@@ -74,7 +77,16 @@ register_lu_kernel(Problem p, int mode)
     constexpr int NRP = NRC * CH > 0 ? NRC * CH : 1;
     constexpr int ROWC = NBC + NRC;
     constexpr int NPIV = (NB + LPM - 1) / LPM;     // pivots recorded per lane
-    constexpr int XC = NR > 0 ? NB * NRC : 1;      // chunks of the staged X
+    // one matrix per wavefront with 512-byte rows and one right-hand side:
+    // B lives in LDS (row i of B at bst row i), not in VGPRs, so that the
+    // kernel fits three wavefronts per SIMD like the factorisation alone;
+    // x_k then overwrites y_k in place and X leaves from there.  (Measured:
+    // complex float n = 64, batch 8192: 0.468 -> 0.407 ms; with 8 or 16
+    // right-hand sides the per-step LDS traffic costs more than the third
+    // wavefront gains, 0.57 -> 0.59 and 0.72 -> 1.08 ms, so those keep B in
+    // VGPRs.)
+    constexpr bool BL = NR == 1 && LPM == 64 && RPL == 1 && reg_chunked<T, NB>();
+    constexpr int XC = (NR > 0 && !BL) ? NB * NRC : 1;      // chunks of the staged X
     constexpr int DGC = NR > 0 ? (2 * NB + CH - 1) / CH : 1;   // chunks of (1/u_jj, u_jj)
     constexpr int VB = RPL * (int)sizeof(T);       // bytes of a lane's rows in one column
     static_assert(NB % CH == 0 && NB % RPL == 0 && LPM <= 64 && 64 % LPM == 0, "bad shape");
@@ -82,6 +94,7 @@ register_lu_kernel(Problem p, int mode)
     __shared__ uint4 rowbuf[GPB][ROWC];
     __shared__ uint4 xstage[GPB][XC];   // X row k at chunks [k*NRC, (k+1)*NRC)
     __shared__ uint4 diagbuf[GPB][DGC]; // (1/u_jj, u_jj) of every step j
+    __shared__ uint4 bst[BL ? GPB * NB * NRC : 1];   // B rows (BL)
 
     const int lane = threadIdx.x & 63;
     const int grp = (threadIdx.x >> 6) * GPW + lane / LPM;
@@ -131,14 +144,30 @@ register_lu_kernel(Problem p, int mode)
             }
         }
     }
+    if constexpr (BL) {
+        // row li of B into its LDS row (zero past nrhs and n)
 #pragma unroll
-    for (int r = 0; r < NRP; ++r) {
+        for (int c = 0; c < NRC; ++c) {
+            T v[CH];
 #pragma unroll
-        for (int s = 0; s < RPL; ++s) {
-            const int row = li * RPL + s;
-            T v = O::zero();
-            if (solve && r < NR && r < p.nrhs && row < n) v = B[row + (long long)r * p.ldb];
-            b[s][r] = v;
+            for (int e = 0; e < CH; ++e) {
+                const int r = c * CH + e;
+                v[e] = (solve && r < NR && r < p.nrhs && li < n) ? B[li + (long long)r * p.ldb] : O::zero();
+            }
+            uint4 w;
+            __builtin_memcpy(&w, v, 16);
+            bst[(grp * NB + li) * NRC + c] = w;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < NRP; ++r) {
+#pragma unroll
+            for (int s = 0; s < RPL; ++s) {
+                const int row = li * RPL + s;
+                T v = O::zero();
+                if (solve && r < NR && r < p.nrhs && row < n) v = B[row + (long long)r * p.ldb];
+                b[s][r] = v;
+            }
         }
     }
 
@@ -164,6 +193,7 @@ register_lu_kernel(Problem p, int mode)
             kmax = kk > kmax ? kk : kmax;
         }
         int piv_pos;
+        int owner = 0;   // lane holding the pivot row (LPM == 64)
         T piv_early = O::zero();
         if constexpr (LPM == 64) {
             // one matrix per wavefront (one row per lane): DPP inside rows
@@ -174,6 +204,7 @@ register_lu_kernel(Problem p, int mode)
             int win;
             wave_argmax(key[0], pos[0], kmax, win);
             win = win < 0 ? 0 : win;
+            owner = win;
             piv_pos = __builtin_amdgcn_readlane(pos[0], win);
             piv_early = readlane_t(a[0][j], win);
         } else {
@@ -197,7 +228,7 @@ register_lu_kernel(Problem p, int mode)
                     __builtin_memcpy(&w, &a[s][c * CH], 16);
                     rowbuf[grp][c] = w;
                 }
-                if constexpr (NRC > 0) {
+                if constexpr (NRC > 0 && !BL) {
                     if (solve) {
 #pragma unroll
                         for (int c = 0; c < NRC; ++c) {
@@ -299,7 +330,30 @@ register_lu_kernel(Problem p, int mode)
                         for (int e = 0; e < CH; ++e)
                             if (c * CH + e > j) O::fms(a[s][c * CH + e], l, uc[e]);
                     }
-                    if constexpr (NR > 0) {
+                    if constexpr (BL) {
+                        if (solve) {
+                            // the pivot row's right-hand sides straight from
+                            // its owner's LDS row; this lane's own row updated
+                            // in place
+                            const uint4* const urow = &bst[(grp * NB + owner) * NRC];
+                            uint4* const brow = &bst[(grp * NB + li) * NRC];
+                            // a chunk at a time (unrolled, the reads would all
+                            // be hoisted and hold registers the factor needs)
+#pragma unroll 1
+                            for (int c = 0; c < NRC; ++c) {
+                                T uc[CH], bc[CH];
+                                uint4 w = urow[c];
+                                __builtin_memcpy(uc, &w, 16);
+                                uint4 v = brow[c];
+                                __builtin_memcpy(bc, &v, 16);
+#pragma unroll
+                                for (int e = 0; e < CH; ++e)
+                                    if (c * CH + e < NR) O::fms(bc[e], l, uc[e]);
+                                __builtin_memcpy(&v, bc, 16);
+                                brow[c] = v;
+                            }
+                        }
+                    } else if constexpr (NR > 0) {
                         if (solve) {
 #pragma unroll
                             for (int c = 0; c < NRC; ++c) {
@@ -323,7 +377,59 @@ register_lu_kernel(Problem p, int mode)
     // normal) for right-hand sides r = li, li + LPM, ..., and stages it; then
     // every row above position k reads x_k back and subtracts u_ik * x_k.
     // Each x_kr is formed once instead of in every lane of the group.
-    if constexpr (NR > 0) {
+    if constexpr (BL) {
+        // y_k is already in the LDS row of the lane at position k: lane r
+        // forms x_kr there in place; after a wavefront sync the rows above
+        // read x_k and update their own LDS rows
+        if (solve) {
+#pragma unroll
+            for (int k = NB - 1; k >= 0; --k) {
+                if (k >= n) continue;
+                const int own = __builtin_ctzll(__builtin_amdgcn_ballot_w64(pos[0] == k));
+                T* const xrow = reinterpret_cast<T*>(&bst[(grp * NB + own) * NRC]);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                {
+                    const T rk = diag[2 * k];
+                    const T dk = diag[2 * k + 1];
+                    const bool tiny = !(O::metric(dk) >= O::sfmin());
+                    if (li < NR) {
+                        const T y = xrow[li];
+                        T x = O::mul(y, rk);
+                        if (__builtin_expect(__builtin_amdgcn_ballot_w64(tiny) != 0, 0)) {
+                            asm volatile("" ::: "memory");
+                            if (tiny) x = O::div(y, dk);
+                        }
+                        xrow[li] = x;
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if (pos[0] < k) {
+                    const uint4* const xr4 = &bst[(grp * NB + own) * NRC];
+                    uint4* const brow = &bst[(grp * NB + li) * NRC];
+#pragma unroll 1
+                    for (int c = 0; c < NRC; ++c) {
+                        T xc[CH], bc[CH];
+                        uint4 w = xr4[c];
+                        __builtin_memcpy(xc, &w, 16);
+                        uint4 v = brow[c];
+                        __builtin_memcpy(bc, &v, 16);
+#pragma unroll
+                        for (int e = 0; e < CH; ++e)
+                            if (c * CH + e < NR) O::fms(bc[e], a[0][k], xc[e]);
+                        __builtin_memcpy(&v, bc, 16);
+                        brow[c] = v;
+                    }
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    } else if constexpr (NR > 0) {
         if (solve) {
             const T* const ybuf = reinterpret_cast<const T*>(&rowbuf[grp][0]);
 #pragma unroll
@@ -398,7 +504,23 @@ register_lu_kernel(Problem p, int mode)
         if (j < n) ipiv[j] = pivrec[t] + 1;
     }
     if (li == 0) p.info[m] = info;
-    if constexpr (NR > 0) {
+    if constexpr (BL) {
+        if (solve && info == 0 && pos[0] < n) {
+            // each lane stores x at the position of the row it holds
+            const uint4* const brow = &bst[(grp * NB + li) * NRC];
+#pragma unroll
+            for (int c = 0; c < NRC; ++c) {
+                T xc[CH];
+                uint4 w = brow[c];
+                __builtin_memcpy(xc, &w, 16);
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    const int r2 = c * CH + e;
+                    if (r2 < NR && r2 < p.nrhs) B[pos[0] + (long long)r2 * p.ldb] = xc[e];
+                }
+            }
+        }
+    } else if constexpr (NR > 0) {
         if (solve && info == 0) {
             // X rows li*RPL .. li*RPL+RPL-1 from the stage
             T xr[RPL][NRP];
