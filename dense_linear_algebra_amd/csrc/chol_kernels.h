@@ -143,8 +143,17 @@ __device__ inline void wave_sync() {
 // ---------------------------------------------------------------------------
 constexpr int kRegWaves = 4;
 
+// Float at NB = 32 (two matrices per wavefront) is budgeted for five
+// wavefronts per SIMD: left alone the compiler takes 98 VGPRs for the
+// nrhs-8 kernel (four per SIMD); with the hint it needs 76 (six) with no
+// spill, and posv n = 32, batch 32768 runs 3 - 16 % faster (nrhs 8: 0.220
+// -> 0.203 ms).  Elsewhere the hint spilled (NB = 64) or was not needed.
 template <typename T, int NB, int NR>
-__global__ void __launch_bounds__(64 * kRegWaves) chol_reg_kernel(Problem p)
+constexpr int chol_reg_waves() { return (sizeof(T) == 4 && NB == 32) ? 5 : 1; }
+
+template <typename T, int NB, int NR>
+__global__ void __launch_bounds__(64 * kRegWaves) __attribute__((amdgpu_waves_per_eu(chol_reg_waves<T, NB, NR>())))
+chol_reg_kernel(Problem p)
 {
     using O = cops<T>;
     using R = typename O::R;
