@@ -45,9 +45,10 @@ constexpr int NT = 256;       // threads per work-group = largest order
 constexpr int NW = NT / 64;   // wavefronts
 // LDS stage for U12: CW trailing columns at a time.  The widest trailing
 // matrix at once where LDS allows; f64 budgeted for three work-groups per
-// compute unit stages 112 columns (three 43 KB work-groups fit the 160 KB).
+// compute unit stages 112 columns (three 43 KB work-groups fit the 160 KB),
+// for four 64 columns (31 KB each).
 template <typename T, int WPE> struct Stage {
-    static constexpr int CW = (sizeof(T) == 8 && WPE >= 3) ? 112 : NT - NB;
+    static constexpr int CW = (sizeof(T) == 8 && WPE >= 4) ? 64 : (sizeof(T) == 8 && WPE >= 3) ? 112 : NT - NB;
     static constexpr int SLD = CW + 8;   // padded against bank conflicts
 };
 
@@ -84,8 +85,9 @@ __device__ inline int mfma_row(int lk, int r) {
 }
 
 // WPE: wavefronts per SIMD the registers are budgeted for (= work-groups per
-// compute unit: f32 4; f64 2 with the full-width stage, or 3 with the
-// 112-column stage: 168 VGPRs, no spill)
+// compute unit: f32 4; f64 2 with the full-width stage, 3 with the 112-column
+// stage (168 VGPRs, no spill), or 4 with the 64-column stage and the pivot
+// row read from LDS in the update (128 VGPRs, a 4-byte spill))
 template <typename T, int WPE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
 lu_fused_kernel(Problem p, uint32_t extent_bytes)
@@ -189,10 +191,16 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
             uint32_t rowaddr = (uint32_t)(uintptr_t)(lds_t*)&cand[buf][vb][0];
             asm volatile("" : "+v"(rowaddr));
             lds_t* row = (lds_t*)(uintptr_t)rowaddr;
-            T u[NB];
+            // the pivot row in registers, except for f64 budgeted for four
+            // work-groups per compute unit, which reads it from LDS in the
+            // update (128 VGPRs leave no room for a second row)
+            constexpr bool ROWREG = !(sizeof(T) == 8 && WPE >= 4);
+            T u[ROWREG ? NB : 1];
+            if constexpr (ROWREG) {
 #pragma unroll
-            for (int c = 0; c < NB; ++c)
-                if (c > jj) u[c] = row[c];
+                for (int c = 0; c < NB; ++c)
+                    if (c > jj) u[c] = row[c];
+            }
             if (pos == ppos) sipiv[j0 + jj] = j0 + ppos;   // the pivot row's owner records it
             pos = (pos == ppos) ? jj : (pos == jj ? ppos : pos);
             const R pm = O::metric(piv);
@@ -226,7 +234,10 @@ lu_fused_kernel(Problem p, uint32_t extent_bytes)
                 a[jj] = l;
 #pragma unroll
                 for (int c = 0; c < NB; ++c)
-                    if (c > jj) O::fms(a[c], l, u[c]);
+                    if (c > jj) {
+                        if constexpr (ROWREG) O::fms(a[c], l, u[c]);
+                        else O::fms(a[c], l, (T)row[c]);
+                    }
             }
         }
         // rows to their final positions; L11 to LDS for the U12 solve
@@ -468,14 +479,18 @@ hipError_t blocked_fused_getrf(int dtype, const Problem& p, hipStream_t s) {
     const uint32_t ext = (uint32_t)extent_of(dtype, p.n, p.lda);
     if (dtype == R32)
         hipLaunchKernelGGL((lu_fused_kernel<float, 4>), dim3((unsigned)p.batch), dim3(NT), 0, s, p, ext);
-    else if (p.n <= 224 || p.batch > 1024)
-        // three work-groups per compute unit: measured 3 - 23 % faster (n = 96 -
-        // 224 at batch 1024 - 4096, n = 256 above batch 1024)
+    else if (p.batch >= 1024)
+        // four work-groups per compute unit once the batch fills them:
+        // measured against three, n = 96 - 256 at batch 2048 - 4096, 2 - 14 %
+        // faster; against two at n = 256, batch 1024, 1.247 -> 1.148 ms
+        hipLaunchKernelGGL((lu_fused_kernel<double, 4>), dim3((unsigned)p.batch), dim3(NT), 0, s, p, ext);
+    else if (p.batch > 512)
+        // three work-groups per unit hold up to 768 matrices at once
         hipLaunchKernelGGL((lu_fused_kernel<double, 3>), dim3((unsigned)p.batch), dim3(NT), 0, s, p, ext);
     else
-        // n = 256 at batch <= 1024: two work-groups per compute unit with the
-        // full-width stage (three per unit leave a partial second round
-        // there; measured 2 % slower)
+        // up to two matrices per compute unit: two work-groups per unit with
+        // the full-width stage (n = 256, batch 512: 0.635 ms against 0.651
+        // with three and 0.742 with four)
         hipLaunchKernelGGL((lu_fused_kernel<double, 2>), dim3((unsigned)p.batch), dim3(NT), 0, s, p, ext);
     return hipGetLastError();
 }

@@ -181,12 +181,13 @@ def test_blocked_full_size_workloads(name):
         assert sr <= 20, f"matrix {b}: solve residual {sr}"
 
 
-@pytest.mark.parametrize("n,batch", [(256, 1100), (200, 700)])
-def test_fused_double_three_per_compute_unit(n, batch):
-    """The double one-work-group kernel budgeted for three work-groups per
-    compute unit (112-column U12 stage: several stage chunks per panel),
-    which serves n <= 224 and batches above 1024: ipiv, info and LU
-    bit-identical to the oracle on matrices spread over the batch."""
+@pytest.mark.parametrize("n,batch", [(256, 1100), (96, 1024), (200, 700)])
+def test_fused_double_three_and_four_per_compute_unit(n, batch):
+    """The double one-work-group kernel budgeted for four work-groups per
+    compute unit (batch >= 1024: 64-column U12 stage, pivot row read from LDS
+    in the panel update) and for three (batch 513 - 1023: 112-column stage):
+    ipiv, info and LU bit-identical to the oracle on matrices spread over
+    the batch."""
     dtype = np.float64
     A, _ = lu_inputs.random_problem(4400 + n, dtype, n, 1, batch)
     print(f"case fused f64 3/CU n={n} batch={batch}", flush=True)
