@@ -68,8 +68,17 @@ __device__ inline bool gen_desc(const GenArgs& g, long long b, GenMat<T>& d) {
            (d.m == 0 || d.n == 0 || (d.A != nullptr && d.ipiv != nullptr));
 }
 
+// Float with one row per thread is budgeted for four wavefronts per SIMD:
+// left alone the compiler takes 131 VGPRs (three per SIMD); at 128 it
+// spills 8 bytes per lane, and the variable-size gesv (n in [16, 256],
+// batch 4096) runs 6.25 -> 5.65 ms.  Two rows per thread spill heavily at
+// three or four per SIMD and keep the default.
 template <typename T, int RPT>
-__global__ void __launch_bounds__(GNT) getrf_general_kernel(GenArgs g)
+constexpr int general_waves() { return (sizeof(T) == 4 && RPT == 1) ? 4 : 1; }
+
+template <typename T, int RPT>
+__global__ void __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(general_waves<T, RPT>())))
+getrf_general_kernel(GenArgs g)
 {
     using O = ops<T>;
     using R = typename O::R;
