@@ -83,7 +83,10 @@ bool lu_composed_wins(int t, int n) {
     switch (t) {
     case BATCHLU_R32: return n <= 8;
     case BATCHLU_R64: return n >= 16;
-    case BATCHLU_C64: return n >= 16 && n <= 32;
+    // complex float: the register tiers' back substitution with one x_k
+    // entry per lane made them the fastest at n = 32 too (0.89 - 0.93 of
+    // the composition's time)
+    case BATCHLU_C64: return false;
     default: return n >= 16;
     }
 }

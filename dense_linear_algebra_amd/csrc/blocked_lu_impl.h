@@ -1331,16 +1331,18 @@ hipError_t launch_update(const Problem& p, int j0, int rest, int c0, int N, hipS
 // own columns (and ipiv, info) and the remaining update only the columns
 // beyond them, so the two touch disjoint data; every element still takes its
 // updates in the same order.  The fork and join cost several microseconds per
-// panel, which pays only while the first trailing update leaves compute units
-// idle: at most one 64-row strip per compute unit (256) over the batch
-// (measured: n = 2048, batch 8 gains 7 %; n = 1024 and 512 at batch 64 lose
-// 3 % and 16 % with it).
+// panel, which pays only for long panels while the first trailing update
+// leaves compute units idle: real types, n >= 1024, at most one 64-row strip
+// per compute unit (256) over the batch (measured: n = 2048, batch 8 gains
+// 7 %; n = 1024 and 512 at batch 64 lose 3 % and 16 %; complex n = 96 - 256
+// at batch <= 64 lose 5 - 15 %).
 template <typename T>
 hipError_t getrf_t(const Problem& p, hipStream_t s) {
     const int n = p.n;
     hipError_t e;
     LookAhead la;
-    const bool ahead = n > 2 * NBP && (long long)((n - NBP + 63) / 64) * p.batch <= 256 && lookahead_begin(la);
+    const bool ahead = !ops<T>::is_complex && n >= 1024 && (long long)((n - NBP + 63) / 64) * p.batch <= 256 &&
+                       lookahead_begin(la);
     if ((e = launch_panel<T>(p, 0, min(NBP, n), s)) != hipSuccess) return lookahead_end(la, e);
     for (int j0 = 0; j0 + NBP < n; j0 += NBP) {
         const int rest = n - j0 - NBP;

@@ -132,6 +132,9 @@ def test_tier_pin_refuses_instead_of_truncating():
     # float n <= 8 with many right-hand sides: LDS tier up to batch 1024
     (lib.R32, 2, 8, 16, 1024, lib.TIER_CTA_LDS),
     (lib.R32, 2, 8, 16, 8192, lib.TIER_TINY),
+    # complex float n = 32 with 16 right-hand sides: the register tier at
+    # every batch
+    (lib.C64, 2, 32, 16, 64, lib.TIER_TINY),
     # getrf keeps the register tiers at every batch
     (lib.R64, 0, 64, 0, 1, lib.TIER_CTA),
     (lib.C64, 0, 16, 0, 16, lib.TIER_TINY),
