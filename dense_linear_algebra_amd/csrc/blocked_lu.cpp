@@ -74,13 +74,12 @@ hipError_t blocked_getri_r64(const Problem& p, hipStream_t s);
 hipError_t blocked_getri_c64(const Problem& p, hipStream_t s);
 hipError_t blocked_getri_c128(const Problem& p, hipStream_t s);
 
+// Every type to n = 4096: panels taller than the register-resident kernels
+// reach stay in memory (the deferred left interchanges hold four rows per
+// thread of 1024).
 bool blocked_supported(int dtype, int n) {
-    // the largest orders the parity tests run: float and double 2048, the
-    // complex types 1024 (double panels above 1024 rows and complex double
-    // panels above 512 rows hold four rows per thread and spill registers:
-    // correct, slower)
-    const int cap = (dtype == R32 || dtype == R64) ? 2048 : 1024;
-    return n >= 1 && n <= cap;
+    (void)dtype;
+    return n >= 1 && n <= 4096;
 }
 
 hipError_t blocked_getrf(int dtype, const Problem& p, hipStream_t s) {

@@ -160,20 +160,205 @@ __global__ void __launch_bounds__(MAXT) panel_kernel(Problem p, int j0, int w)
     }
 }
 
-// Four wavefronts, RPT rows per thread (row = tid + 256 q), ONE work-group
-// barrier per column: each wavefront finds its argmax (rows of a lane first,
-// then DPP and readlane across lanes) and publishes key, position and
-// candidate row to a double-buffered LDS slot; every thread reads the four
-// slots and picks the winner.  Fewer, fuller wavefronts than one row per
-// thread: the per-step overhead (reduction, exchange, reciprocal) is paid by
-// four wavefronts instead of up to sixteen.
-template <typename T, int RPT>
-__global__ void __launch_bounds__(256) panel4_kernel(Problem p, int j0, int w)
+// Panels taller than the register-resident kernels reach (at most 4096 rows,
+// 1024 threads with up to four rows each): the panel stays in memory, where
+// this work-group's own earlier column steps left it (32 columns, L2-resident),
+// and each column step reads and updates it there.  Rows keep their storage
+// places while the panel is factored; pos[] follows each row's position after
+// the interchanges so far, as in the register kernels, and the rows that moved
+// go to their final positions at the end.  Per element the operations are
+// those of the register kernels: l = a * (1 / pivot) (a / pivot when the
+// pivot is below the safe minimum), then a_c -= l u_c column by column, one
+// column step at a time.  Two barriers per step: one after the per-wavefront
+// argmax, one after the update (the next step reads what this one wrote).
+template <typename T>
+__global__ void __launch_bounds__(1024) panel_mem_kernel(Problem p, int j0, int w)
 {
     using O = ops<T>;
     using R = typename O::R;
     using K = typename O::K;
-    constexpr int NT = 256, NW = 4;
+    constexpr int NT = 1024, NWV = NT / 64, RPT = 4;
+    constexpr int CH = sizeof(T) >= 16 ? 2 : sizeof(T) == 8 ? 4 : 8;   // columns per load batch
+    const int m = p.n - j0;                 // panel height (<= NT * RPT)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const long long mat = blockIdx.x;
+    const long long lda = p.lda;
+
+    __shared__ K skey[NWV];
+    __shared__ int spos[NWV];
+    __shared__ int sphy[NWV];
+    __shared__ int srec[NBP];
+
+    T* A = (T*)p.A + mat * p.sA + j0 + (long long)j0 * lda;   // panel origin
+
+    // element (r, c) of the panel: column c's base (uniform) plus the row's
+    // byte offset (32-bit, one register per row for every column)
+    auto at = [](T* col, unsigned boff) -> T& { return *(T*)((char*)col + boff); };
+    // the offsets, re-read in each iteration: hoisted 64-bit addresses per
+    // row and column would not fit the registers
+    auto fresh = [](unsigned v) {
+        asm volatile("" : "+v"(v));
+        return v;
+    };
+    int pos[RPT];
+    unsigned roff[RPT];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+        const int r = tid + q * NT;
+        pos[q] = r < m ? r : 0x3fffffff;
+        roff[q] = (unsigned)r * (unsigned)sizeof(T);
+    }
+
+    int info = 0;
+#pragma unroll 1
+    for (int jj = 0; jj < w; ++jj) {
+        T* colj = A + (long long)jj * lda;     // uniform column bases, unsigned row offsets
+        // a1: the lane's best row (highest key, lowest position among equal
+        // keys), then the wavefront's, then the work-group's
+        K key = 0;
+        int kp = 0x7fffffff, kr = 0;
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            const int r = tid + q * NT;
+            if (pos[q] >= jj && pos[q] < m) {
+                const K kq = (K)pivot_key(O::metric(at(colj, fresh(roff[q]))));
+                if (kq > key || (kq == key && pos[q] < kp)) {
+                    key = kq;
+                    kp = pos[q];
+                    kr = r;
+                }
+            }
+        }
+        K kmax;
+        int win;
+        wave_argmax(key, kp, kmax, win);
+        const int wl = win < 0 ? 0 : win;
+        const int wpos = __builtin_amdgcn_readlane(kp, wl);
+        const int wphy = __builtin_amdgcn_readlane(kr, wl);
+        if (lane == 0) {
+            skey[wave] = win < 0 ? (K)0 : kmax;
+            spos[wave] = win < 0 ? 0x7fffffff : wpos;
+            sphy[wave] = wphy;
+        }
+        __syncthreads();
+        K best = 0;
+        int ppos = 0x7fffffff, pphy = 0;
+#pragma unroll
+        for (int v = 0; v < NWV; ++v) {
+            const K kv = skey[v];
+            const int pv = spos[v];
+            if (kv > best || (kv == best && pv < ppos)) {
+                best = kv;
+                ppos = pv;
+                pphy = sphy[v];
+            }
+        }
+        if (tid == 0) srec[jj] = ppos;
+#pragma unroll
+        for (int q = 0; q < RPT; ++q)
+            pos[q] = (pos[q] == ppos) ? jj : (pos[q] == jj ? ppos : pos[q]);
+        const unsigned prow = (unsigned)pphy * (unsigned)sizeof(T);   // the pivot row, in its storage place
+        const T piv = at(colj, prow);
+        const R pm = O::metric(piv);
+        const bool zero = pm == R(0);
+        if (zero && info == 0) info = j0 + jj + 1;
+        if (!zero) {
+            const T rcp = O::recip(piv);
+            const bool small = !(pm >= O::sfmin());
+            bool act[RPT];
+            T l[RPT];
+#pragma unroll
+            for (int q = 0; q < RPT; ++q) {
+                act[q] = pos[q] > jj && pos[q] < m;
+                if (act[q]) {
+                    const unsigned ro = fresh(roff[q]);
+                    const T a = at(colj, ro);
+                    l[q] = small ? O::div(a, piv) : O::mul(a, rcp);
+                    at(colj, ro) = l[q];
+                }
+            }
+            // a4: columns jj+1 .. w-1, CH at a time (their loads issued
+            // together, ahead of the stores)
+#pragma unroll 1
+            for (int c0 = jj + 1; c0 < w; c0 += CH) {
+                T u[CH], x[RPT][CH];
+                unsigned ro[RPT];
+#pragma unroll
+                for (int q = 0; q < RPT; ++q) ro[q] = fresh(roff[q]);
+                T* cols[CH];
+#pragma unroll
+                for (int cc = 0; cc < CH; ++cc) cols[cc] = A + (long long)(c0 + cc) * lda;
+#pragma unroll
+                for (int cc = 0; cc < CH; ++cc)
+                    if (c0 + cc < w) u[cc] = at(cols[cc], prow);
+#pragma unroll
+                for (int q = 0; q < RPT; ++q)
+#pragma unroll
+                    for (int cc = 0; cc < CH; ++cc)
+                        if (act[q] && c0 + cc < w) x[q][cc] = at(cols[cc], ro[q]);
+#pragma unroll
+                for (int q = 0; q < RPT; ++q)
+#pragma unroll
+                    for (int cc = 0; cc < CH; ++cc)
+                        if (act[q] && c0 + cc < w) {
+                            O::fms(x[q][cc], l[q], u[cc]);
+                            at(cols[cc], ro[q]) = x[q][cc];
+                        }
+            }
+        }
+        __syncthreads();
+    }
+    // the rows that moved go to their final positions, a few columns at a
+    // time: every read of a batch of columns precedes every write to it
+    constexpr int CW = 32 / sizeof(T);
+#pragma unroll 1
+    for (int c0 = 0; c0 < w; c0 += CW) {
+        T v[RPT][CW];
+        T* cols[CW];
+#pragma unroll
+        for (int cc = 0; cc < CW; ++cc) cols[cc] = A + (long long)(c0 + cc) * lda;
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            const int r = tid + q * NT;
+#pragma unroll
+            for (int cc = 0; cc < CW; ++cc)
+                if (r < m && pos[q] != r && c0 + cc < w) v[q][cc] = at(cols[cc], fresh(roff[q]));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+            const int r = tid + q * NT;
+#pragma unroll
+            for (int cc = 0; cc < CW; ++cc)
+                if (r < m && pos[q] != r && c0 + cc < w)
+                    at(cols[cc], (unsigned)pos[q] * (unsigned)sizeof(T)) = v[q][cc];
+        }
+        __syncthreads();
+    }
+    if (tid < w) p.ipiv[mat * p.sP + j0 + tid] = j0 + srec[tid] + 1;
+    if (tid == 0) {
+        int* ip = p.info + mat;
+        if (j0 == 0) *ip = info;
+        else if (info != 0 && *ip == 0) *ip = info;
+    }
+}
+
+// NW wavefronts (four or eight), RPT rows per thread (row = tid + 64 NW q),
+// ONE work-group barrier per column: each wavefront finds its argmax (rows of
+// a lane first, then DPP and readlane across lanes) and publishes key,
+// position and candidate row to a double-buffered LDS slot; every thread reads
+// the NW slots and picks the winner.  Fewer, fuller wavefronts than one row
+// per thread: the per-step overhead (reduction, exchange, reciprocal) is paid
+// by four or eight wavefronts instead of up to sixteen.
+template <typename T, int RPT, int NW = 4>
+__global__ void __launch_bounds__(64 * NW) panel4_kernel(Problem p, int j0, int w)
+{
+    using O = ops<T>;
+    using R = typename O::R;
+    using K = typename O::K;
+    constexpr int NT = 64 * NW;
     const int m = p.n - j0;                 // panel height
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1221,21 +1406,37 @@ template <typename T>
 hipError_t launch_panel(const Problem& p, int j0, int w, hipStream_t s) {
     constexpr int CAP = panel_cap<T>();
     const int m = p.n - j0;
-    // four wavefronts with up to four rows per thread while the rows fit in
-    // registers (real types to 1024 rows, complex float to 512)
+    // four wavefronts with up to two rows per thread to 512 rows; real types
+    // then eight wavefronts, two rows per thread to 1024 rows (float: four to
+    // 2048).  Measured against four wavefronts with four rows: getrf n = 1024,
+    // batch 64, 3.78 ms against 3.97 (float), 6.27 against 6.48 (double);
+    // float n = 2048, batch 16, 8.83 against 9.77 (1024 threads, two rows each)
     if constexpr (sizeof(T) <= 8) {
-        constexpr int CAP4 = ops<T>::is_complex ? 512 : 1024;
+        constexpr int CAP4 = ops<T>::is_complex ? 512 : sizeof(T) == 4 ? 2048 : 1024;
         if (m <= CAP4) {
             if (m <= 256) hipLaunchKernelGGL((panel4_kernel<T, 1>), dim3(p.batch), dim3(256), 0, s, p, j0, w);
             else if (m <= 512) hipLaunchKernelGGL((panel4_kernel<T, 2>), dim3(p.batch), dim3(256), 0, s, p, j0, w);
-            else if constexpr (!ops<T>::is_complex)
-                hipLaunchKernelGGL((panel4_kernel<T, 4>), dim3(p.batch), dim3(256), 0, s, p, j0, w);
+            else if constexpr (!ops<T>::is_complex) {
+                if (m <= 1024)
+                    hipLaunchKernelGGL((panel4_kernel<T, 2, 8>), dim3(p.batch), dim3(512), 0, s, p, j0, w);
+                else if constexpr (sizeof(T) == 4)
+                    hipLaunchKernelGGL((panel4_kernel<T, 4, 8>), dim3(p.batch), dim3(512), 0, s, p, j0, w);
+            }
             return hipGetLastError();
         }
     }
     int nt = ((m + 63) / 64) * 64;
     if (nt > CAP) nt = CAP;
     const int rpt = (m + nt - 1) / nt;
+    // beyond the registers the panel stays in memory (up to 4096 rows); for
+    // complex double also where four rows a thread would spill (measured:
+    // n = 1024, batch 32: 13.5 ms against 15.2; for the other types the
+    // spilling register panel stays faster, by 3 - 30 %)
+    if (rpt > (sizeof(T) >= 16 ? 2 : 4)) {
+        if (m > 4096) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((panel_mem_kernel<T>), dim3(p.batch), dim3(1024), 0, s, p, j0, w);
+        return hipGetLastError();
+    }
     if (nt <= 256) {
         if (rpt <= 1) hipLaunchKernelGGL((panel_kernel<T, 1, 256>), dim3(p.batch), dim3(nt), 0, s, p, j0, w);
         else if (rpt <= 2) hipLaunchKernelGGL((panel_kernel<T, 2, 256>), dim3(p.batch), dim3(nt), 0, s, p, j0, w);

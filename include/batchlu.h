@@ -64,7 +64,7 @@ typedef enum {
 /*
  * batchlu_getrf -- LU with partial pivoting of `batch` n x n matrices, in place.
  *   1 t        data type
- *   2 n        order, n >= 0
+ *   2 n        order, 0 <= n <= 4096 (larger n returns BATCHLU_ERR_CAPACITY)
  *   3 A        device, in: the matrices; out: L (unit diagonal not stored)
  *              below the diagonal and U on and above it, rows in pivoted order
  *   4 lda      >= max(1, n)
@@ -106,7 +106,7 @@ int batchlu_getrs(batchlu_dtype t, char trans, int n, int nrhs, const void* A,
 
 /*
  * batchlu_gesv -- factor and solve: getrf on A, then getrs on B.
- *   1 t, 2 n, 3 nrhs, 4 A, 5 lda, 6 strideA, 7 ipiv, 8 strideP,
+ *   1 t, 2 n (<= 4096, else BATCHLU_ERR_CAPACITY), 3 nrhs, 4 A, 5 lda, 6 strideA, 7 ipiv, 8 strideP,
  *   9 B, 10 ldb, 11 strideB, 12 info, 13 batch, 14 stream.
  * A matrix with info[b] > 0 keeps its B unchanged (LAPACK gesv behaviour).
  * Follows: BatchLAS "LU" page, gesv rows of the family table (a fused

@@ -173,15 +173,16 @@ def test_zero_pivot_factors_through_the_blocked_solve(dtype, n):
     assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
 
 
-# largest order of each blocked configuration, a small batch each
+# the largest orders whose panels fit the registers of one work-group with
+# four rows per thread (complex double: two), a small batch each
 CAPACITY = [(np.float32, 2048), (np.float64, 2048), (np.complex64, 1024), (np.complex128, 1024)]
 
 
 @pytest.mark.parametrize("dtype,n", CAPACITY, ids=lambda v: getattr(v, "__name__", str(v)))
-def test_blocked_tier_at_its_largest_order(dtype, n):
-    """The largest order the blocked tier accepts for each type: ipiv, info
-    and LU bit-identical to the oracle, X bit-identical to the oracle's
-    solve, and one order more is refused with BATCHLU_ERR_CAPACITY."""
+def test_blocked_tier_at_large_orders(dtype, n):
+    """ipiv, info and LU bit-identical to the oracle, X bit-identical to the
+    oracle's solve; the blocked tier's limit, n = 4096 for every type, is
+    accepted and one order more is refused with BATCHLU_ERR_CAPACITY."""
     batch, nrhs = 1, 2
     A, B = lu_inputs.random_problem(7000 + n, dtype, n, nrhs, batch)
     print(f"case capacity {np.dtype(dtype).name} n={n}", flush=True)
@@ -192,4 +193,5 @@ def test_blocked_tier_at_its_largest_order(dtype, n):
     assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
     assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
     t = lib.dtype_code(np.dtype(dtype))
-    assert lib.batchlu_select_tier(t, 0, n + 1, 0, 1) == -101   # BATCHLU_ERR_CAPACITY
+    assert lib.batchlu_select_tier(t, 0, 4096, 0, 1) == lib.TIER_BLOCKED
+    assert lib.batchlu_select_tier(t, 0, 4097, 0, 1) == -101   # BATCHLU_ERR_CAPACITY
