@@ -1293,58 +1293,56 @@ __global__ void __launch_bounds__(256) gemm_valu_kernel(const void* Am, int lda_
 
 // ---------------------------------------------------------------------------
 // deferred left interchanges: after the last panel, the L columns of every
-// panel k are gathered through the interchanges of all later steps.
+// panel k are gathered through the interchanges of all later steps.  One
+// work-group per (matrix, panel): each of its rows at or below the first
+// later step finds its source by tracing itself back through those steps
+// (LDS copy of ipiv), then the panel's columns move a few at a time, every
+// read of a round before any write of it.
 // ---------------------------------------------------------------------------
 template <typename T, int RPT>
-__global__ void __launch_bounds__(1024) left_swap_kernel(Problem p)
+__global__ void __launch_bounds__(1024) left_swap_kernel(Problem p, int npan)
 {
-    extern __shared__ int sipiv[];   // n entries, 0-based
+    extern __shared__ int sipiv[];   // steps lo .. n-1, 0-based rows
     const int n = p.n;
     const int tid = threadIdx.x, nt = blockDim.x;
-    const long long mat = blockIdx.x;
+    const long long mat = blockIdx.x / npan;
+    const int k = (int)(blockIdx.x % npan);        // panel
+    const int lo = (k + 1) * NBP;                   // first row the later steps touch
     T* A = (T*)p.A + mat * p.sA;
-    for (int i = tid; i < n; i += nt) sipiv[i] = p.ipiv[mat * p.sP + i] - 1;
+    for (int i = lo + tid; i < n; i += nt) sipiv[i - lo] = p.ipiv[mat * p.sP + i] - 1;
     __syncthreads();
-    const int P = (n + NBP - 1) / NBP;
     int map[RPT];
 #pragma unroll
-    for (int q = 0; q < RPT; ++q) map[q] = tid + q * nt;
-    for (int k = P - 2; k >= 0; --k) {
-        const int lo = (k + 1) * NBP;                   // first row the later steps touch
-        const int hi = min(n, lo + NBP);                // steps of panel k + 1
+    for (int q = 0; q < RPT; ++q) {
+        const int i = lo + tid + q * nt;
+        int x = i;
+        if (i < n)
+            for (int s = n - 1; s >= lo; --s) {
+                const int ps = sipiv[s - lo];
+                x = (x == s) ? ps : (x == ps ? s : x);
+            }
+        map[q] = x;
+    }
+    const int c0 = k * NBP;
+    constexpr int CC = 8;   // columns per read/write round
+    for (int cb = 0; cb < NBP; cb += CC) {
+        T v[RPT][CC];
 #pragma unroll
         for (int q = 0; q < RPT; ++q) {
-            int x = map[q];
-            if (tid + q * nt >= lo && tid + q * nt < n)
-                for (int s = hi - 1; s >= lo; --s) {
-                    const int ps = sipiv[s];
-                    x = (x == s) ? ps : (x == ps ? s : x);
-                }
-            map[q] = x;
+            const int i = lo + tid + q * nt;
+#pragma unroll
+            for (int c = 0; c < CC; ++c)
+                if (i < n && map[q] != i) v[q][c] = A[map[q] + (long long)(c0 + cb + c) * p.lda];
         }
-        const int c0 = k * NBP, w = min(NBP, n - c0);
-        constexpr int CC = 8;   // columns per read/write round
-        for (int cb = 0; cb < w; cb += CC) {
-            T v[RPT][CC];
+        __syncthreads();
 #pragma unroll
-            for (int q = 0; q < RPT; ++q) {
-                const int i = tid + q * nt;
+        for (int q = 0; q < RPT; ++q) {
+            const int i = lo + tid + q * nt;
 #pragma unroll
-                for (int c = 0; c < CC; ++c)
-                    if (i >= lo && i < n && cb + c < w && map[q] != i)
-                        v[q][c] = A[map[q] + (long long)(c0 + cb + c) * p.lda];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int q = 0; q < RPT; ++q) {
-                const int i = tid + q * nt;
-#pragma unroll
-                for (int c = 0; c < CC; ++c)
-                    if (i >= lo && i < n && cb + c < w && map[q] != i)
-                        A[i + (long long)(c0 + cb + c) * p.lda] = v[q][c];
-            }
-            __syncthreads();
+            for (int c = 0; c < CC; ++c)
+                if (i < n && map[q] != i) A[i + (long long)(c0 + cb + c) * p.lda] = v[q][c];
         }
+        __syncthreads();
     }
 }
 
@@ -1562,12 +1560,16 @@ hipError_t getrf_t(const Problem& p, hipStream_t s) {
         if ((e = lookahead_join_wait(la, s)) != hipSuccess) return lookahead_end(la, e);
     }
     if (n > NBP) {
-        const int nt = panel_threads(n);
-        const int rpt = (n + nt - 1) / nt;
-        const size_t smem = (size_t)n * sizeof(int);
-        if (rpt <= 1) hipLaunchKernelGGL((left_swap_kernel<T, 1>), dim3(p.batch), dim3(nt), smem, s, p);
-        else if (rpt <= 2) hipLaunchKernelGGL((left_swap_kernel<T, 2>), dim3(p.batch), dim3(nt), smem, s, p);
-        else if (rpt <= 4) hipLaunchKernelGGL((left_swap_kernel<T, 4>), dim3(p.batch), dim3(nt), smem, s, p);
+        // panels 0 .. npan-1 have later steps; rows lo .. n-1 of panel k,
+        // at most n - NBP of them
+        const int npan = (n - 1) / NBP;
+        const int nt = panel_threads(n - NBP);
+        const int rpt = (n - NBP + nt - 1) / nt;
+        const size_t smem = (size_t)(n - NBP) * sizeof(int);
+        const dim3 grid((unsigned)((long long)npan * p.batch));
+        if (rpt <= 1) hipLaunchKernelGGL((left_swap_kernel<T, 1>), grid, dim3(nt), smem, s, p, npan);
+        else if (rpt <= 2) hipLaunchKernelGGL((left_swap_kernel<T, 2>), grid, dim3(nt), smem, s, p, npan);
+        else if (rpt <= 4) hipLaunchKernelGGL((left_swap_kernel<T, 4>), grid, dim3(nt), smem, s, p, npan);
         else return lookahead_end(la, hipErrorInvalidValue);
         if ((e = hipGetLastError()) != hipSuccess) return lookahead_end(la, e);
     }
