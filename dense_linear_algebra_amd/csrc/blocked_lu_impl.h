@@ -1316,15 +1316,25 @@ __global__ void __launch_bounds__(1024) left_swap_kernel(Problem p, int npan)
     for (int q = 0; q < RPT; ++q) {
         const int i = lo + tid + q * nt;
         int x = i;
-        if (i < n)
-            for (int s = n - 1; s >= lo; --s) {
+        if (i < n) {
+            // eight steps per round: their LDS reads are in flight together
+            int s = n - 1;
+            for (; s - 7 >= lo; s -= 8) {
+                int ps[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) ps[u] = sipiv[s - u - lo];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x = (x == s - u) ? ps[u] : (x == ps[u] ? s - u : x);
+            }
+            for (; s >= lo; --s) {
                 const int ps = sipiv[s - lo];
                 x = (x == s) ? ps : (x == ps ? s : x);
             }
+        }
         map[q] = x;
     }
     const int c0 = k * NBP;
-    constexpr int CC = 8;   // columns per read/write round
+    constexpr int CC = RPT >= 4 ? 4 : 8;   // columns per read/write round (four rows a thread: 4, no spill)
     for (int cb = 0; cb < NBP; cb += CC) {
         T v[RPT][CC];
 #pragma unroll
@@ -1532,16 +1542,17 @@ hipError_t launch_update(const Problem& p, int j0, int rest, int c0, int N, hipS
 // updates in the same order.  The fork and join cost several microseconds per
 // panel, which pays only for long panels while the first trailing update
 // leaves compute units idle: real types, n >= 1024, at most one 64-row strip
-// per compute unit (256) over the batch (measured: n = 2048, batch 8 gains
-// 7 %; n = 1024 and 512 at batch 64 lose 3 % and 16 %; complex n = 96 - 256
-// at batch <= 64 lose 5 - 15 %).
+// per compute unit (256) over the batch, two from n = 1536 (measured: n =
+// 2048, batch 8 gains 7 %, batch 16 8 % (double 4 %); n = 1536, batch 16
+// 3 %; n = 1024 at batch 32 loses 6 %, n = 1024 and 512 at batch 64 lose 3 %
+// and 16 %; complex n = 96 - 256 at batch <= 64 lose 5 - 15 %).
 template <typename T>
 hipError_t getrf_t(const Problem& p, hipStream_t s) {
     const int n = p.n;
     hipError_t e;
     LookAhead la;
-    const bool ahead = !ops<T>::is_complex && n >= 1024 && (long long)((n - NBP + 63) / 64) * p.batch <= 256 &&
-                       lookahead_begin(la);
+    const long long strips = (long long)((n - NBP + 63) / 64) * p.batch;
+    const bool ahead = !ops<T>::is_complex && n >= 1024 && strips <= (n >= 1536 ? 512 : 256) && lookahead_begin(la);
     if ((e = launch_panel<T>(p, 0, min(NBP, n), s)) != hipSuccess) return lookahead_end(la, e);
     for (int j0 = 0; j0 + NBP < n; j0 += NBP) {
         const int rest = n - j0 - NBP;

@@ -199,3 +199,18 @@ def test_fused_double_three_and_four_per_compute_unit(n, batch):
         assert gI[b] == oI[0]
         np.testing.assert_array_equal(gP[b, :n], oP[0])
         assert np.array_equal(bits(gA[sl]), bits(oA))
+
+
+@pytest.mark.parametrize("dtype,n,batch", [(np.float32, 1600, 12), (np.float64, 1540, 12)],
+                         ids=lambda v: getattr(v, "__name__", str(v)))
+def test_lookahead_from_1536_rows(dtype, n, batch):
+    """From n = 1536 the next panel runs on the look-ahead stream up to two
+    64-row strips per compute unit over the batch (here 25 x 12 and 24 x 12):
+    LU, ipiv and info bit-identical to the oracle."""
+    A, _ = lu_inputs.random_problem(7700 + n, dtype, n, 1, batch)
+    print(f"case look-ahead {np.dtype(dtype).name} n={n} batch={batch}", flush=True)
+    gA, _, gP, gI = gesv_gpu(lib, A, None, n, 0, batch, op="getrf")
+    oA, _, oP, oI, _ = oracle_run(A, None, n, 0, batch, op="getrf")
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
