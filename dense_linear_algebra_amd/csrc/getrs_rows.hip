@@ -470,14 +470,16 @@ hipError_t getrs_rows_launch(int dtype, const Problem& p, hipStream_t s) {
         default: return hipErrorInvalidValue;
         }
     }
-    // orders to 256 with many right-hand sides: wider tiles stream the
-    // factors fewer times while the batch still gives enough work-groups
-    // (measured, solve alone: double n = 256, nrhs = 16, batch 1024 0.70 ->
-    // 0.42 ms; complex double n = 128, nrhs = 16 0.58 -> 0.36; float n = 256
-    // 0.38 -> 0.34).  Not above 256 (equal or slower), not for complex float
-    // (up to 2x slower), and not where a tile would be half empty (double
-    // n = 64 with 8 right-hand sides in 16-wide tiles: 0.27 -> 0.40 ms).
-    if (p.n <= 256) {
+    // orders to 256 with many right-hand sides and batches of 512 or more:
+    // wider tiles stream the factors fewer times while the batch still gives
+    // enough work-groups (measured, solve alone: double n = 256, nrhs = 16,
+    // batch 1024 0.70 -> 0.42 ms; complex double n = 128, nrhs = 16 0.58 ->
+    // 0.36; float n = 256 0.38 -> 0.34).  Not above 256 (equal or slower),
+    // not for complex float (up to 2x slower), not at batch <= 256 (the gesv
+    // that factors then solves, double n = 32 - 64 with 16 right-hand sides,
+    // went 27 - 43 % slower), and not where a tile would be half empty
+    // (double n = 64 with 8 right-hand sides in 16-wide tiles: 0.27 -> 0.40 ms).
+    if (p.n <= 256 && p.batch >= 512) {
         if ((dtype == R32 || dtype == R64) && r > 8)
             return dtype == R32 ? launch_t<float, 16>(p, s) : launch_t<double, 16>(p, s);
         if (dtype == C128 && r > 4) return launch_t<cplx<double>, 8>(p, s);
