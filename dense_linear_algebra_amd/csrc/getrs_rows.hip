@@ -36,6 +36,21 @@ constexpr int CK = 16;   // columns of L or U loaded per round
 template <typename T, int NRT>
 constexpr int pf_count() { return (sizeof(T) == 8 && !ops<T>::is_complex && NRT <= 4) ? CK : 0; }
 
+// Work-group -> (matrix, RHS tile).  Work-groups are dealt to the eight
+// XCDs in turn; when the batch is a multiple of eight, the tiles of one
+// matrix go to one XCD, so they read its factors through one L2.
+__device__ inline void tile_of(int batch, int rtiles, long long& m, int& tile) {
+    const unsigned b = blockIdx.x;
+    if (rtiles > 1 && (batch & 7) == 0) {
+        const unsigned slot = b >> 3;
+        m = (long long)(slot / (unsigned)rtiles) * 8 + (b & 7);
+        tile = (int)(slot % (unsigned)rtiles);
+    } else {
+        m = b / (unsigned)rtiles;
+        tile = (int)(b % (unsigned)rtiles);
+    }
+}
+
 // IDENT: getri.  B is not read; the right-hand sides are the identity's
 // columns, so row `row` of P*I is e_src (one where the column is src).
 template <typename T, int NRT, bool IDENT>
@@ -47,8 +62,10 @@ __global__ void __launch_bounds__(1024) getrs_rows_kernel(Problem p, int rtiles)
     T* ybuf = (T*)((char*)smem_raw + ((p.n * 4 + 15) / 16) * 16);            // [2][BS][NRT]
 
     const int n = p.n;
-    const long long m = blockIdx.x / rtiles;
-    const int c0 = (int)(blockIdx.x % rtiles) * NRT;
+    long long m;
+    int c0;
+    tile_of(p.batch, rtiles, m, c0);
+    c0 *= NRT;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -277,8 +294,10 @@ __global__ void __launch_bounds__(1024) getrs_rows_trans_kernel(Problem p, int r
     T* ybuf = (T*)((char*)smem_raw + ((p.n * 4 + 15) / 16) * 16);            // [2][BS][NRT]
 
     const int n = p.n;
-    const long long m = blockIdx.x / rtiles;
-    const int c0 = (int)(blockIdx.x % rtiles) * NRT;
+    long long m;
+    int c0;
+    tile_of(p.batch, rtiles, m, c0);
+    c0 *= NRT;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
