@@ -920,6 +920,21 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const void* Am, int lda_
             }
 }
 
+// Work-group -> (matrix, strip).  Work-groups are dealt to the eight XCDs in
+// turn; when the batch is a multiple of eight, the strips of one matrix go
+// to one XCD, so they read its U12 through one L2.
+__device__ inline void strip_of(int mstrips, long long& mat, int& strip) {
+    const unsigned b = blockIdx.x, batch = gridDim.x / (unsigned)mstrips;
+    if (mstrips > 1 && (batch & 7) == 0) {
+        const unsigned slot = b >> 3;
+        mat = (long long)(slot / (unsigned)mstrips) * 8 + (b & 7);
+        strip = (int)(slot % (unsigned)mstrips);
+    } else {
+        mat = b / (unsigned)mstrips;
+        strip = (int)(b % (unsigned)mstrips);
+    }
+}
+
 // getrf trailing update A22 -= L21 U12 (real types, K = 32, ascending k): one
 // work-group per 64-row strip of one matrix walks the strip's 64-column
 // tiles.  L21 stays in registers as MFMA operands for the whole strip; the
@@ -941,8 +956,10 @@ __global__ void __launch_bounds__(256) update_strip_kernel(T* A, int lda, long l
     __shared__ __attribute__((aligned(16))) T Us[2][NBP][UP];
     __shared__ unsigned zmask;
     const int tid = threadIdx.x;
-    const long long mat = blockIdx.x / mstrips;
-    const int r0 = (int)(blockIdx.x % mstrips) * 64;
+    long long mat;
+    int r0;
+    strip_of(mstrips, mat, r0);
+    r0 *= 64;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wc = wave >> 1;
     const int li = lane & 15, lk = lane >> 4;
@@ -1089,8 +1106,10 @@ __global__ void __launch_bounds__(256) update_strip_cplx_kernel(cplx<R>* A, int 
     __shared__ __attribute__((aligned(16))) T Us[2][NBP][UP];
     __shared__ unsigned zmask;
     const int tid = threadIdx.x;
-    const long long mat = blockIdx.x / mstrips;
-    const int r0 = (int)(blockIdx.x % mstrips) * SH;
+    long long mat;
+    int r0;
+    strip_of(mstrips, mat, r0);
+    r0 *= SH;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wc = wave >> 1;
     const int li = lane & 15, lk = lane >> 4;

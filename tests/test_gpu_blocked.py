@@ -214,3 +214,20 @@ def test_lookahead_from_1536_rows(dtype, n, batch):
     np.testing.assert_array_equal(gI, oI)
     np.testing.assert_array_equal(gP[:, :n], oP)
     assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+
+
+@pytest.mark.parametrize("dtype,n", [(np.float32, 300), (np.float64, 290), (np.complex64, 130), (np.complex128, 100)],
+                         ids=lambda v: getattr(v, "__name__", str(v)))
+def test_batch_multiple_of_eight(dtype, n):
+    """A batch that is a multiple of eight maps the trailing-update strips
+    (and the solve's right-hand-side tiles) of one matrix to one XCD: LU,
+    ipiv, info and X bit-identical to the oracle."""
+    batch, nrhs = 16, 12
+    A, B = lu_inputs.random_problem(7900 + n, dtype, n, nrhs, batch)
+    print(f"case batch 16 {np.dtype(dtype).name} n={n}", flush=True)
+    gA, gB, gP, gI = gesv_gpu(lib, A, B, n, nrhs, batch, op="getrf+getrs")
+    oA, oB, oP, oI, _ = oracle_run(A, B, n, nrhs, batch, op="getrf+getrs")
+    np.testing.assert_array_equal(gI, oI)
+    np.testing.assert_array_equal(gP[:, :n], oP)
+    assert matrices_equal_bits(gA, oA, n, n, n, n * n, batch) == []
+    assert matrices_equal_bits(gB, oB, n, nrhs, n, n * nrhs, batch) == []
