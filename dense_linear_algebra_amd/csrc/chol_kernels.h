@@ -372,6 +372,22 @@ __device__ inline int mfma_row(int lk, int r) {
     return sizeof(R) == 4 ? 4 * lk + r : lk + 4 * r;
 }
 
+// Work-group -> (matrix, part) for grids of `per` work-groups per matrix.
+// Work-groups are dealt to the eight XCDs in turn; when the batch is a
+// multiple of eight, the parts of one matrix go to one XCD, so the data they
+// share (the panel, the factor) comes through one L2.
+__device__ inline void chol_part_of(int per, long long& mat, int& part) {
+    const unsigned b = blockIdx.x, batch = gridDim.x / (unsigned)per;
+    if (per > 1 && (batch & 7) == 0) {
+        const unsigned slot = b >> 3;
+        mat = (long long)(slot / (unsigned)per) * 8 + (b & 7);
+        part = (int)(slot % (unsigned)per);
+    } else {
+        mat = b / (unsigned)per;
+        part = (int)(b % (unsigned)per);
+    }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) chol_syrk_kernel(Problem p, int j0, int mstrips)
 {
@@ -380,9 +396,11 @@ __global__ void __launch_bounds__(256) chol_syrk_kernel(Problem p, int j0, int m
     constexpr int UPAD = 64 + (sizeof(T) == 4 ? 4 : 2);
     __shared__ __attribute__((aligned(16))) T Us[2][NBP][UPAD];
     const int tid = threadIdx.x;
-    const long long mat = blockIdx.x / mstrips;
+    long long mat;
+    int r0;
+    chol_part_of(mstrips, mat, r0);
+    r0 *= 64;
     if (p.info[mat] != 0) return;
-    const int r0 = (int)(blockIdx.x % mstrips) * 64;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wc = wave >> 1;
     const int li = lane & 15, lk = lane >> 4;
@@ -510,9 +528,11 @@ __global__ void __launch_bounds__(256) chol_herk_kernel(Problem p, int j0, int m
     constexpr int UPAD = 64 + (sizeof(R) == 4 ? 2 : 1);
     __shared__ __attribute__((aligned(16))) T Us[2][NBP][UPAD];
     const int tid = threadIdx.x;
-    const long long mat = blockIdx.x / mstrips;
+    long long mat;
+    int r0;
+    chol_part_of(mstrips, mat, r0);
+    r0 *= SH;
     if (p.info[mat] != 0) return;
-    const int r0 = (int)(blockIdx.x % mstrips) * SH;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave & 1, wc = wave >> 1;
     const int li = lane & 15, lk = lane >> 4;
@@ -659,8 +679,10 @@ __global__ void __launch_bounds__(1024) chol_solve_kernel(Problem p, int rtiles)
     using O = cops<T>;
     __shared__ T ybuf[2][BS][NRT];
     const int n = p.n;
-    const long long m = blockIdx.x / rtiles;
-    const int c0 = (int)(blockIdx.x % rtiles) * NRT;
+    long long m;
+    int c0;
+    chol_part_of(rtiles, m, c0);
+    c0 *= NRT;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;

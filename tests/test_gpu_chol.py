@@ -139,6 +139,25 @@ def test_posv_matches_oracle(tier, dtype, n, nrhs, uplo):
 
 
 @pytest.mark.parametrize("uplo", ["L", "U"])
+@pytest.mark.parametrize("dtype,n", [(np.float32, 200), (np.float64, 300), (np.complex64, 130), (np.complex128, 100)],
+                         ids=lambda v: getattr(v, "__name__", str(v)))
+def test_blocked_posv_batch_multiple_of_eight(dtype, n, uplo):
+    """A batch that is a multiple of eight maps the trailing-update strips and
+    the solve's right-hand-side tiles of one matrix to one XCD: the factor and
+    X bit-identical to the oracle's."""
+    lib.batchlu_set_tier(TIERS["blocked"])
+    batch, nrhs = 16, 12
+    A, B = lu_inputs.spd_problem(2500 + n, dtype, n, nrhs, batch)
+    A, mask = _poison_other(A, n, batch, uplo)
+    gA, gB, gI = _posv_gpu(A, B, n, nrhs, batch, uplo)
+    oA, oB = A.copy(), B.copy()
+    oI, _ = oracle.posv(oA, n, n, n * n, oB, nrhs, n, n * nrhs, batch, uplo=uplo)
+    np.testing.assert_array_equal(gI, oI)
+    _check_factor(gA, oA, n, batch, oI, uplo, mask, A)
+    assert np.array_equal(bits(gB), bits(oB)), "X differs from the oracle"
+
+
+@pytest.mark.parametrize("uplo", ["L", "U"])
 @pytest.mark.parametrize("dtype,n,nrhs", [(np.float32, 40, 4), (np.float64, 300, 3), (np.complex64, 129, 1),
                                           (np.complex128, 64, 5), (np.float32, 1000, 2)],
                          ids=lambda v: getattr(v, "__name__", str(v)))
