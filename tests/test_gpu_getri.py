@@ -44,6 +44,22 @@ CASES = ([(np.float32, n) for n in (1, 5, 32, 33, 64, 100, 257)]
          + [(np.complex128, n) for n in (17, 63)])
 
 
+@pytest.mark.parametrize("dtype,n", [(np.float32, 70), (np.complex128, 40)],
+                         ids=lambda v: getattr(v, "__name__", str(v)))
+def test_getri_batch_multiple_of_eight(dtype, n):
+    """A batch that is a multiple of eight maps the column tiles of one
+    matrix's inverse to one XCD: C bit-identical to the oracle's."""
+    batch = 16
+    A, _ = lu_inputs.random_problem(9450 + n, dtype, n, 0, batch)
+    print(f"case getri batch 16 {np.dtype(dtype).name} n={n}", flush=True)
+    gA, _, gP, gI = gesv_gpu(lib, A, None, n, 0, batch, op="getrf")
+    assert not gI.any()
+    gC = _getri_gpu(gA, gP[:, :n], np.zeros(batch * n * n, dtype), n, batch, n, n * n, n, n * n, n)
+    oC = np.zeros(batch * n * n, dtype)
+    oracle.getri(gA, n, n, n * n, gP[:, :n], oC, n, n * n, batch)
+    assert matrices_equal_bits(gC, oC, n, n, n, n * n, batch) == []
+
+
 @pytest.mark.parametrize("dtype,n", CASES, ids=lambda v: getattr(v, "__name__", str(v)))
 def test_getri_matches_oracle_bitwise(dtype, n):
     batch = 3
