@@ -673,6 +673,28 @@ __global__ void __launch_bounds__(256) chol_herk_kernel(Problem p, int j0, int m
 // ---------------------------------------------------------------------------
 constexpr int BS = 32;
 
+// x_k = y_k / l_kk for the NRT right-hand sides held by diagonal lane dl,
+// broadcast in xc (lane dl keeps them in y): lane r divides right-hand side
+// r by the broadcast real diagonal (the same operands, so the same bits), so
+// the wavefront pays for one division per step rather than NRT.
+template <typename O, typename T, int NRT>
+__device__ inline void chol_diag_divide(T (&y)[NRT], T (&xc)[NRT], typename O::R diag, int dl, int lane) {
+    T yc[NRT];
+#pragma unroll
+    for (int r = 0; r < NRT; ++r) yc[r] = readlane_t(y[r], dl);
+    const typename O::R d = readlane_t(diag, dl);
+    T v = yc[0];
+#pragma unroll
+    for (int r = 1; r < NRT; ++r)
+        if (lane == r) v = yc[r];
+    const T q = O::divr(v, d);
+#pragma unroll
+    for (int r = 0; r < NRT; ++r) xc[r] = readlane_t(q, r);
+    if (lane == dl)
+#pragma unroll
+        for (int r = 0; r < NRT; ++r) y[r] = xc[r];
+}
+
 template <typename T, int NRT>
 __global__ void __launch_bounds__(1024) chol_solve_kernel(Problem p, int rtiles)
 {
@@ -713,12 +735,13 @@ __global__ void __launch_bounds__(1024) chol_solve_kernel(Problem p, int rtiles)
 #pragma unroll
             for (int c = 0; c < BS; ++c) {
                 if (c >= w) continue;
-                if (mrow == c)
-#pragma unroll
-                    for (int r = 0; r < NRT; ++r) y[r] = O::divr(y[r], O::re(lrow[c]));
                 T xc[NRT];
-#pragma unroll
-                for (int r = 0; r < NRT; ++r) xc[r] = readlane_t(y[r], base + c);
+                if constexpr (NRT == 1) {
+                    if (mrow == c) y[0] = O::divr(y[0], O::re(lrow[c]));
+                    xc[0] = readlane_t(y[0], base + c);
+                } else {
+                    chol_diag_divide<O>(y, xc, O::re(lrow[c]), base + c, lane);
+                }
                 if (inb && mrow > c)
 #pragma unroll
                     for (int r = 0; r < NRT; ++r) O::fms(y[r], lrow[c], xc[r]);
@@ -755,12 +778,13 @@ __global__ void __launch_bounds__(1024) chol_solve_kernel(Problem p, int rtiles)
 #pragma unroll
             for (int c = BS - 1; c >= 0; --c) {
                 if (c >= w) continue;
-                if (mrow == c)
-#pragma unroll
-                    for (int r = 0; r < NRT; ++r) y[r] = O::divr(y[r], O::re(lcol[c]));
                 T xc[NRT];
-#pragma unroll
-                for (int r = 0; r < NRT; ++r) xc[r] = readlane_t(y[r], base + c);
+                if constexpr (NRT == 1) {
+                    if (mrow == c) y[0] = O::divr(y[0], O::re(lcol[c]));
+                    xc[0] = readlane_t(y[0], base + c);
+                } else {
+                    chol_diag_divide<O>(y, xc, O::re(lcol[c]), base + c, lane);
+                }
                 if (inb && mrow < c)
 #pragma unroll
                     for (int r = 0; r < NRT; ++r) O::fms_cx(y[r], lcol[c], xc[r]);
