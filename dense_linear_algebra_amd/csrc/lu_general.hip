@@ -319,6 +319,29 @@ getrf_general_kernel(GenArgs g)
 // unit-lower L and back with U (true division by u_kk) a 32-row block at a
 // time, NRT right-hand sides per pass.  With info given, matrices whose
 // info is not 0 keep their B.
+// x_c = y_c / u_cc for the NRT right-hand sides held by diagonal lane dl,
+// broadcast in xc (lane dl keeps them in y): lane r divides right-hand side
+// r by the broadcast diagonal (the same operands, so the same bits), so the
+// wavefront pays for one division per step rather than NRT.
+template <typename T, int NRT>
+__device__ inline void spread_divide(T (&y)[NRT], T (&xc)[NRT], T diag, int dl, int lane) {
+    using O = ops<T>;
+    T yc[NRT];
+#pragma unroll
+    for (int r = 0; r < NRT; ++r) yc[r] = readlane_t(y[r], dl);
+    const T d = readlane_t(diag, dl);
+    T v = yc[0];
+#pragma unroll
+    for (int r = 1; r < NRT; ++r)
+        if (lane == r) v = yc[r];
+    const T q = O::div(v, d);
+#pragma unroll
+    for (int r = 0; r < NRT; ++r) xc[r] = readlane_t(q, r);
+    if (lane == dl)
+#pragma unroll
+        for (int r = 0; r < NRT; ++r) y[r] = xc[r];
+}
+
 template <typename T, int NRT>
 __global__ void __launch_bounds__(1024) getrs_general_kernel(GenArgs g, const int* nrhs_arr,
                                                             void* const* Bptrs, const int* ldbs, int check_info)
@@ -395,12 +418,13 @@ __global__ void __launch_bounds__(1024) getrs_general_kernel(GenArgs g, const in
                 for (int c = BS - 1; c >= 0; --c) {
                     if (c >= wd) continue;
                     const T uv = (inb && mrow <= c) ? F[row + (long long)(r0 + c) * lda] : O::zero();
-                    if (mrow == c)
-#pragma unroll
-                        for (int r = 0; r < NRT; ++r) y[r] = O::div(y[r], uv);
                     T xc[NRT];
-#pragma unroll
-                    for (int r = 0; r < NRT; ++r) xc[r] = readlane_t(y[r], base + c);
+                    if constexpr (NRT == 1) {
+                        if (mrow == c) y[0] = O::div(y[0], uv);
+                        xc[0] = readlane_t(y[0], base + c);
+                    } else {
+                        spread_divide(y, xc, uv, base + c, lane);
+                    }
                     if (inb && mrow < c)
 #pragma unroll
                         for (int r = 0; r < NRT; ++r) O::fms(y[r], uv, xc[r]);
